@@ -1,0 +1,835 @@
+// libhe runtime: context, state machine, KV workspace, decode-graph cache and the
+// C ABI declared in include/he.h.
+//
+// One context is one model instance (paper summary, "The DeepSpeed Hybrid Engine:
+// Architecture and Mode Switching": the engine keeps a single copy of the actor and
+// reconfigures it at the eval()/train() boundary).  Inference layout here means: the
+// LoRA adapters folded into the weights in place, and a KV workspace allocated
+// (page 2, section 3: fuse before generate, unfuse after; release the workspace
+// after generation, re-take it before the next).  The decode step can be replayed
+// from a captured hipGraph (page 2, section 4: enable_cuda_graph), with the step's
+// position kept in device memory so that one graph serves every step.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/he.h"
+#include "kernels.h"
+
+#ifndef HE_BUILD_FLAGS
+#define HE_BUILD_FLAGS "unknown"
+#endif
+
+using namespace he;
+
+namespace {
+
+constexpr int kMaxDecodeBatch = 128;   // decode GEMM keeps <= 8 MFMA column tiles
+
+struct Timer {
+  bool armed = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> live;   // recorded, not yet read
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;   // free
+  std::vector<double> bytes, flops;
+  he_kernel_stat acc{0, 0.0, 0.0, 0.0};
+};
+
+size_t esize(int dt) { return dt == DT_BF16 ? 2 : 4; }
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+struct he_ctx {
+  he_model_desc desc{};
+  he_weight_table wt{};
+  std::vector<he_layer_weights> layers;
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+  int dt = DT_BF16, L = 0, d = 0, H = 0, D = 0, F = 0, V = 0, de = 0;
+  float q_scale = 1.f;
+  bool validate_only = false, use_graph = true;
+  bool fused = false, failed = false;
+  std::string err;
+
+  // workspace (library-owned)
+  bool cache = false;
+  int max_batch = 0, max_seq = 0, bpad = 0, rows = 0;
+  void* kv = nullptr;
+  size_t kv_layer_elems = 0;     // elements of one [B_max][H][S_max][D] block
+  char* scratch = nullptr;
+  float* h = nullptr;
+  void* x = nullptr;
+  void* xe = nullptr;
+  void* q = nullptr;
+  void* o = nullptr;
+  void* a = nullptr;
+  float* parts = nullptr;
+  float* logits = nullptr;
+  float* best_val = nullptr;
+  int32_t* best_idx = nullptr;
+  int32_t* ids_cur = nullptr;
+  int32_t* tokens = nullptr;
+  int32_t* pos_dev = nullptr;
+  int n_argmax_blocks = 0;
+  int split_qkv = 1, split_out = 1, split_fc2 = 1;
+
+  // cache epoch
+  bool prefilled = false;
+  int cur_B = 0, cur_pos = 0;
+
+  // decode graphs: [0] without logits, [1] with logits, for batch graph_B
+  hipGraphExec_t graph[2] = {nullptr, nullptr};
+  int graph_B = -1;
+  bool capturing = false;
+
+  Timer timers[HE_K_COUNT];
+  bool fail_next_alloc = false, fail_next_step = false;
+};
+
+// ------------------------------------------------------------------------------------
+// helpers
+// ------------------------------------------------------------------------------------
+static he_status set_err(he_ctx* c, he_status s, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+  }
+  return s;
+}
+
+static he_status hip_fail(he_ctx* c, hipError_t e, const char* what) {
+  c->failed = true;
+  return set_err(c, HE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(c, call)                                   \
+  do {                                                     \
+    hipError_t e_ = (call);                                \
+    if (e_ != hipSuccess) return hip_fail((c), e_, #call); \
+  } while (0)
+
+// After a batch of launches: surface launch errors.
+static he_status check_launch(he_ctx* c, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(c, e, what);
+  return HE_OK;
+}
+
+static void* kcache(he_ctx* c, int l) {
+  return (char*)c->kv + (size_t)(2 * l) * c->kv_layer_elems * esize(c->dt);
+}
+static void* vcache(he_ctx* c, int l) {
+  return (char*)c->kv + (size_t)(2 * l + 1) * c->kv_layer_elems * esize(c->dt);
+}
+
+// Run one launch, bracketed by events when its kernel class is armed.
+template <class Fn>
+static void run_k(he_ctx* c, int kclass, double bytes, double flops, Fn&& fn) {
+  Timer& t = c->timers[kclass];
+  if (!t.armed || c->capturing) {
+    fn();
+    return;
+  }
+  std::pair<hipEvent_t, hipEvent_t> ev;
+  if (!t.pool.empty()) {
+    ev = t.pool.back();
+    t.pool.pop_back();
+  } else {
+    if (hipEventCreate(&ev.first) != hipSuccess || hipEventCreate(&ev.second) != hipSuccess) {
+      fn();
+      return;
+    }
+  }
+  hipEventRecord(ev.first, c->stream);
+  fn();
+  hipEventRecord(ev.second, c->stream);
+  t.live.push_back(ev);
+  t.bytes.push_back(bytes);
+  t.flops.push_back(flops);
+}
+
+static bool any_timer_armed(const he_ctx* c) {
+  for (const Timer& t : c->timers)
+    if (t.armed) return true;
+  return false;
+}
+
+static int gemv_splits(int N, int K) {
+  const int nb = (N + 63) / 64;
+  const int steps = K / 32;
+  int s = (512 + nb - 1) / nb;
+  s = std::min(s, std::max(1, steps / 8));
+  return std::max(1, s);
+}
+
+static void drop_graphs(he_ctx* c) {
+  for (auto& g : c->graph)
+    if (g) {
+      hipGraphExecDestroy(g);
+      g = nullptr;
+    }
+  c->graph_B = -1;
+}
+
+// ------------------------------------------------------------------------------------
+// enqueue sequences
+// ------------------------------------------------------------------------------------
+static const void* ln_g_after(he_ctx* c, int l) {   // norm applied before layer l+1's attention
+  return (l + 1 < c->L) ? c->layers[l + 1].ln1_g : c->wt.lnf_g;
+}
+static const void* ln_b_after(he_ctx* c, int l) {
+  return (l + 1 < c->L) ? c->layers[l + 1].ln1_b : c->wt.lnf_b;
+}
+
+// Prompt pass of a pre-LN LM-head model; leaves z (final LN of the last rows) in x.
+static void enqueue_prefill_lm(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
+  const int M = B * S, d = c->d, F = c->F, dt = c->dt;
+  const float eps = c->desc.ln_eps;
+  const size_t es = esize(dt);
+  hipStream_t st = c->stream;
+  run_k(c, HE_K_EMBED_NORM, (double)M * d * (2 * es + 4 + es), 0, [&] {
+    launch_embed_norm(dt, ids, nullptr, S, c->wt.tok_emb, c->wt.pos_emb,
+                      c->L ? c->layers[0].ln1_g : c->wt.lnf_g, c->L ? c->layers[0].ln1_b : c->wt.lnf_b,
+                      eps, c->h, c->x, M, d, c->V, st);
+  });
+  for (int l = 0; l < c->L; ++l) {
+    const he_layer_weights& w = c->layers[l];
+    EpiArgs e;
+    e.mode = EPI_QKV;
+    e.bias = w.b_qkv;
+    e.q_out = c->q;
+    e.k_cache = kcache(c, l);
+    e.v_cache = vcache(c, l);
+    e.d = d; e.H = c->H; e.D = c->D; e.S_max = c->max_seq; e.seq_len = S; e.pos0 = 0;
+    e.q_scale = c->q_scale;
+    run_k(c, HE_K_GEMM_PREFILL, (double)3 * d * d * es, 2.0 * M * 3 * d * d,
+          [&] { launch_gemm(dt, c->x, w.w_qkv, M, 3 * d, d, e, st); });
+    run_k(c, HE_K_ATTN_PREFILL, (double)M * d * es * 4, 2.0 * B * d * (double)S * (S + 1),
+          [&] { launch_attn_prefill(dt, c->q, kcache(c, l), vcache(c, l), c->o, B, S, c->H, c->D, c->max_seq, st); });
+    EpiArgs r;
+    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h;
+    run_k(c, HE_K_GEMM_PREFILL, (double)d * d * es, 2.0 * M * d * d,
+          [&] { launch_gemm(dt, c->o, w.w_out, M, d, d, r, st); });
+    run_k(c, HE_K_EMBED_NORM, (double)M * d * (4 + es), 0, [&] {
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, st);
+    });
+    EpiArgs f1;
+    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a;
+    run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
+          [&] { launch_gemm(dt, c->x, w.w_fc1, M, F, d, f1, st); });
+    EpiArgs f2;
+    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h;
+    run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
+          [&] { launch_gemm(dt, c->a, w.w_fc2, M, d, F, f2, st); });
+    if (l + 1 < c->L)
+      run_k(c, HE_K_EMBED_NORM, (double)M * d * (4 + es), 0, [&] {
+        launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[l + 1].ln1_g, c->layers[l + 1].ln1_b,
+                    eps, c->x, M, d, 1, 0, 0, st);
+      });
+  }
+  // final LayerNorm of the last prompt position only
+  run_k(c, HE_K_EMBED_NORM, (double)B * d * (4 + es), 0, [&] {
+    launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, S, S - 1, 0, st);
+  });
+  GemvArgs g;
+  g.out_mode = GV_ARGMAX;
+  g.logits = want_logits ? c->logits : nullptr;
+  g.best_val = c->best_val;
+  g.best_idx = c->best_idx;
+  g.n_blocks = c->n_argmax_blocks;
+  g.bump = c->pos_dev;
+  run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d,
+        [&] { launch_gemv(dt, c->x, c->wt.tok_emb, B, c->V, d, g, st); });
+  launch_argmax_finalize(c->best_val, c->best_idx, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
+                         c->max_seq + 1, c->pos_dev, nullptr, st);
+}
+
+// One decode step for batch B: feeds ids_cur at *pos_dev.  Host mirror `pos` is
+// only used for the timers' byte counts.
+static void enqueue_step(he_ctx* c, int B, bool want_logits, int pos) {
+  const int d = c->d, F = c->F, dt = c->dt;
+  const float eps = c->desc.ln_eps;
+  const size_t es = esize(dt);
+  hipStream_t st = c->stream;
+  run_k(c, HE_K_EMBED_NORM, (double)B * d * (2 * es + 4 + es), 0, [&] {
+    launch_embed_norm(dt, c->ids_cur, c->pos_dev, 1, c->wt.tok_emb, c->wt.pos_emb,
+                      c->L ? c->layers[0].ln1_g : c->wt.lnf_g, c->L ? c->layers[0].ln1_b : c->wt.lnf_b,
+                      eps, c->h, c->x, B, d, c->V, st);
+  });
+  for (int l = 0; l < c->L; ++l) {
+    const he_layer_weights& w = c->layers[l];
+    GemvArgs gq;
+    gq.out_mode = GV_PARTIAL; gq.splits = c->split_qkv; gq.parts = c->parts;
+    run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * es, 2.0 * B * 3 * d * d,
+          [&] { launch_gemv(dt, c->x, w.w_qkv, B, 3 * d, d, gq, st); });
+    run_k(c, HE_K_ATTN_DECODE, 2.0 * B * d * es * (double)(pos + 1), 4.0 * B * d * (double)(pos + 1), [&] {
+      launch_attn_decode(dt, c->parts, c->split_qkv, w.b_qkv, kcache(c, l), vcache(c, l), c->pos_dev,
+                         c->o, B, c->H, c->D, c->max_seq, c->q_scale, st);
+    });
+    GemvArgs go;
+    go.out_mode = GV_PARTIAL; go.splits = c->split_out; go.parts = c->parts;
+    run_k(c, HE_K_GEMV_DECODE, (double)d * d * es, 2.0 * B * d * d,
+          [&] { launch_gemv(dt, c->o, w.w_out, B, d, d, go, st); });
+    run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
+      launch_norm(dt, c->h, c->parts, c->split_out, w.b_out, w.ln2_g, w.ln2_b, eps, c->x, B, d, 1, 0, 0, st);
+    });
+    GemvArgs g1;
+    g1.out_mode = GV_RELU; g1.bias = w.b_fc1; g1.out = c->a;
+    run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
+          [&] { launch_gemv(dt, c->x, w.w_fc1, B, F, d, g1, st); });
+    GemvArgs g2;
+    g2.out_mode = GV_PARTIAL; g2.splits = c->split_fc2; g2.parts = c->parts;
+    run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
+          [&] { launch_gemv(dt, c->a, w.w_fc2, B, d, F, g2, st); });
+    run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
+      launch_norm(dt, c->h, c->parts, c->split_fc2, w.b_fc2, ln_g_after(c, l), ln_b_after(c, l), eps,
+                  c->x, B, d, 1, 0, 0, st);
+    });
+  }
+  if (c->L == 0)
+    run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
+      launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, 1, 0, 0, st);
+    });
+  GemvArgs g;
+  g.out_mode = GV_ARGMAX;
+  g.logits = want_logits ? c->logits : nullptr;
+  g.best_val = c->best_val;
+  g.best_idx = c->best_idx;
+  g.n_blocks = c->n_argmax_blocks;
+  g.bump = c->pos_dev;
+  run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d,
+        [&] { launch_gemv(dt, c->x, c->wt.tok_emb, B, c->V, d, g, st); });
+  launch_argmax_finalize(c->best_val, c->best_idx, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
+                         c->max_seq + 1, c->pos_dev, nullptr, st);
+}
+
+// Full causal pass of a scalar-head model, reward at the last position.
+static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* reward) {
+  const int M = B * S, d = c->d, F = c->F, dt = c->dt, de = c->de;
+  const float eps = c->desc.ln_eps;
+  const size_t es = esize(dt);
+  const bool post = c->desc.norm == HE_NORM_POST;
+  hipStream_t st = c->stream;
+  if (de != d) {
+    launch_embed_gather(dt, ids, c->wt.tok_emb, c->xe, M, de, c->V, st);
+    EpiArgs e;
+    e.mode = EPI_POSADD; e.pos_emb = c->wt.pos_emb; e.h = c->h; e.out = c->x; e.seq_len = S; e.pos0 = 0;
+    run_k(c, HE_K_GEMM_PREFILL, (double)d * de * es, 2.0 * M * d * de,
+          [&] { launch_gemm(dt, c->xe, c->wt.proj_in, M, d, de, e, st); });
+    if (!post && c->L)
+      launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[0].ln1_g, c->layers[0].ln1_b, eps, c->x, M, d,
+                  1, 0, 0, st);
+  } else {
+    launch_embed_norm(dt, ids, nullptr, S, c->wt.tok_emb, c->wt.pos_emb,
+                      (!post && c->L) ? c->layers[0].ln1_g : nullptr,
+                      (!post && c->L) ? c->layers[0].ln1_b : nullptr, eps, c->h, c->x, M, d, c->V, st);
+  }
+  for (int l = 0; l < c->L; ++l) {
+    const he_layer_weights& w = c->layers[l];
+    EpiArgs e;
+    e.mode = EPI_QKV; e.bias = w.b_qkv; e.q_out = c->q; e.k_cache = kcache(c, l); e.v_cache = vcache(c, l);
+    e.d = d; e.H = c->H; e.D = c->D; e.S_max = c->max_seq; e.seq_len = S; e.pos0 = 0; e.q_scale = c->q_scale;
+    run_k(c, HE_K_GEMM_PREFILL, (double)3 * d * d * es, 2.0 * M * 3 * d * d,
+          [&] { launch_gemm(dt, c->x, w.w_qkv, M, 3 * d, d, e, st); });
+    run_k(c, HE_K_ATTN_PREFILL, (double)M * d * es * 4, 2.0 * B * d * (double)S * (S + 1),
+          [&] { launch_attn_prefill(dt, c->q, kcache(c, l), vcache(c, l), c->o, B, S, c->H, c->D, c->max_seq, st); });
+    EpiArgs r;
+    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h;
+    run_k(c, HE_K_GEMM_PREFILL, (double)d * d * es, 2.0 * M * d * d,
+          [&] { launch_gemm(dt, c->o, w.w_out, M, d, d, r, st); });
+    if (post)
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln1_g, w.ln1_b, eps, c->x, M, d, 1, 0, 1, st);
+    else
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, st);
+    EpiArgs f1;
+    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a;
+    run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
+          [&] { launch_gemm(dt, c->x, w.w_fc1, M, F, d, f1, st); });
+    EpiArgs f2;
+    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h;
+    run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
+          [&] { launch_gemm(dt, c->a, w.w_fc2, M, d, F, f2, st); });
+    if (post)
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 1, st);
+    else if (l + 1 < c->L)
+      launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[l + 1].ln1_g, c->layers[l + 1].ln1_b, eps, c->x,
+                  M, d, 1, 0, 0, st);
+  }
+  int xs = S;
+  if (!post) {   // pre-LN: final LayerNorm of the last position
+    launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, S, S - 1, 0, st);
+    xs = 1;
+  }
+  run_k(c, HE_K_SCORE, (double)de * d * es, 2.0 * B * de * d,
+        [&] { launch_score(dt, c->x, c->wt.proj_out, c->wt.score_w, reward, B, xs, d, de, st); });
+}
+
+// ------------------------------------------------------------------------------------
+// C ABI
+// ------------------------------------------------------------------------------------
+extern "C" {
+
+const char* he_status_str(he_status s) {
+  switch (s) {
+    case HE_OK: return "HE_OK";
+    case HE_E_ARG: return "HE_E_ARG";
+    case HE_E_STATE: return "HE_E_STATE";
+    case HE_E_NOCACHE: return "HE_E_NOCACHE";
+    case HE_E_RANGE: return "HE_E_RANGE";
+    case HE_E_OOM: return "HE_E_OOM";
+    case HE_E_HIP: return "HE_E_HIP";
+    case HE_E_UNSUPPORTED: return "HE_E_UNSUPPORTED";
+    default: return "HE_E_UNKNOWN";
+  }
+}
+
+const char* he_last_error(const he_ctx* c) { return c ? c->err.c_str() : ""; }
+
+const char* he_build_info(void) { return "libhe gfx950 " HE_BUILD_FLAGS; }
+
+he_status he_create(const he_model_desc* desc, const he_weight_table* w, void* hip_stream,
+                    he_ctx** out) {
+  if (!desc || !w || !out) return HE_E_ARG;
+  *out = nullptr;
+  const he_model_desc& D = *desc;
+  if (D.tp_size != 1) return HE_E_UNSUPPORTED;
+  if (D.n_layers < 0 || D.d_model <= 0 || D.n_heads <= 0 || D.d_ffn <= 0 || D.vocab <= 0 ||
+      D.max_pos <= 0 || D.d_model % D.n_heads != 0 || !(D.ln_eps >= 0.f))
+    return HE_E_ARG;
+  if (D.dtype != HE_DTYPE_F32 && D.dtype != HE_DTYPE_BF16) return HE_E_ARG;
+  if (D.norm != HE_NORM_PRE && D.norm != HE_NORM_POST) return HE_E_ARG;
+  if (D.head != HE_HEAD_LM && D.head != HE_HEAD_SCALAR) return HE_E_ARG;
+  const int de = D.d_embed ? D.d_embed : D.d_model;
+  const int hd = D.d_model / D.n_heads;
+  const bool bf = D.dtype == HE_DTYPE_BF16;
+  if (bf ? !(hd == 32 || hd == 64 || hd == 128) : !(hd == 16 || hd == 32 || hd == 64 || hd == 128))
+    return HE_E_UNSUPPORTED;
+  if (D.d_model % 32 || D.d_ffn % 32 || de % 32 || D.d_model > 8192) return HE_E_UNSUPPORTED;
+  if (D.head == HE_HEAD_LM && (D.norm != HE_NORM_PRE || de != D.d_model)) return HE_E_UNSUPPORTED;
+  if (!w->tok_emb || !w->pos_emb || (D.n_layers > 0 && !w->layers)) return HE_E_ARG;
+  if (D.norm == HE_NORM_PRE && (!w->lnf_g || !w->lnf_b)) return HE_E_ARG;
+  if (de != D.d_model && (!w->proj_in || (D.head == HE_HEAD_SCALAR && !w->proj_out))) return HE_E_ARG;
+  if (D.head == HE_HEAD_SCALAR && !w->score_w) return HE_E_ARG;
+  for (int l = 0; l < D.n_layers; ++l) {
+    const he_layer_weights& lw = w->layers[l];
+    const void* p[] = {lw.ln1_g, lw.ln1_b, lw.w_qkv, lw.b_qkv, lw.w_out, lw.b_out,
+                       lw.ln2_g, lw.ln2_b, lw.w_fc1, lw.b_fc1, lw.w_fc2, lw.b_fc2};
+    for (const void* q : p)
+      if (!q) return HE_E_ARG;
+  }
+
+  he_ctx* c = new (std::nothrow) he_ctx();
+  if (!c) return HE_E_OOM;
+  c->desc = D;
+  c->wt = *w;
+  c->layers.assign(w->layers, w->layers + D.n_layers);
+  c->wt.layers = c->layers.data();
+  c->dt = bf ? DT_BF16 : DT_F32;
+  c->L = D.n_layers; c->d = D.d_model; c->H = D.n_heads; c->D = hd; c->F = D.d_ffn; c->V = D.vocab;
+  c->de = de;
+  c->q_scale = (float)(1.0 / std::sqrt((double)hd));
+  c->validate_only = (D.flags & HE_FLAG_VALIDATE_ONLY) != 0;
+  const char* ng = std::getenv("HE_NO_GRAPH");
+  c->use_graph = D.use_graph && !(ng && ng[0] == '1');
+  c->split_qkv = gemv_splits(3 * c->d, c->d);
+  c->split_out = gemv_splits(c->d, c->d);
+  c->split_fc2 = gemv_splits(c->d, c->F);
+  c->n_argmax_blocks = gemv_argmax_blocks(c->dt, c->V);
+  if (!c->validate_only) {
+    if (hip_stream) {
+      c->stream = (hipStream_t)hip_stream;
+    } else {
+      hipError_t e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
+      if (e != hipSuccess) {
+        delete c;
+        return HE_E_HIP;
+      }
+      c->own_stream = true;
+    }
+  }
+  *out = c;
+  return HE_OK;
+}
+
+he_status he_release_cache(he_ctx* c) {
+  if (!c) return HE_E_ARG;
+  drop_graphs(c);
+  if (!c->cache) return HE_OK;
+  if (!c->validate_only) {
+    hipError_t e1 = hipStreamSynchronize(c->stream);
+    hipError_t e2 = c->kv ? hipFree(c->kv) : hipSuccess;
+    hipError_t e3 = c->scratch ? hipFree(c->scratch) : hipSuccess;
+    c->kv = nullptr;
+    c->scratch = nullptr;
+    c->cache = false;
+    c->prefilled = false;
+    if (e1 != hipSuccess) return hip_fail(c, e1, "hipStreamSynchronize");
+    if (e2 != hipSuccess) return hip_fail(c, e2, "hipFree(kv)");
+    if (e3 != hipSuccess) return hip_fail(c, e3, "hipFree(scratch)");
+  }
+  c->cache = false;
+  c->prefilled = false;
+  return HE_OK;
+}
+
+he_status he_destroy(he_ctx* c) {
+  if (!c) return HE_OK;
+  he_status s = he_release_cache(c);
+  if (!c->validate_only) {
+    for (Timer& t : c->timers) {
+      for (auto& p : t.live) { hipEventDestroy(p.first); hipEventDestroy(p.second); }
+      for (auto& p : t.pool) { hipEventDestroy(p.first); hipEventDestroy(p.second); }
+    }
+    if (c->own_stream) hipStreamDestroy(c->stream);
+  }
+  delete c;
+  return s;
+}
+
+static he_status lora_common(he_ctx* c, const he_lora_table* t, float sign) {
+  if (!t || !t->pairs) return set_err(c, HE_E_ARG, "NULL LoRA table");
+  if (t->rank < 1 || t->rank > 64) return set_err(c, HE_E_ARG, "LoRA rank %d outside 1..64", t->rank);
+  if (!std::isfinite(t->alpha)) return set_err(c, HE_E_ARG, "LoRA alpha not finite");
+  for (int i = 0; i < c->L * HE_N_PROJ; ++i)
+    if ((t->pairs[i].A == nullptr) != (t->pairs[i].B == nullptr))
+      return set_err(c, HE_E_ARG, "LoRA pair %d has only one factor", i);
+  if (c->validate_only) return HE_OK;
+  const float s = t->alpha / (float)t->rank;
+  const int d = c->d, F = c->F, r = t->rank;
+  const size_t es = esize(c->dt);
+  for (int l = 0; l < c->L; ++l) {
+    const he_layer_weights& w = c->layers[l];
+    for (int p = 0; p < HE_N_PROJ; ++p) {
+      const he_lora_pair& pr = t->pairs[l * HE_N_PROJ + p];
+      if (!pr.A) continue;
+      void* W;
+      int N, K;
+      switch (p) {
+        case HE_PROJ_Q: W = w.w_qkv; N = d; K = d; break;
+        case HE_PROJ_K: W = (char*)w.w_qkv + (size_t)d * d * es; N = d; K = d; break;
+        case HE_PROJ_V: W = (char*)w.w_qkv + (size_t)2 * d * d * es; N = d; K = d; break;
+        case HE_PROJ_OUT: W = w.w_out; N = d; K = d; break;
+        case HE_PROJ_FC1: W = w.w_fc1; N = F; K = d; break;
+        default: W = w.w_fc2; N = d; K = F; break;
+      }
+      run_k(c, HE_K_LORA, 2.0 * N * K * es + (double)(N + K) * r * es, 2.0 * N * K * r,
+            [&] { launch_lora(c->dt, W, pr.A, pr.B, N, K, r, s, sign, c->stream); });
+    }
+  }
+  return check_launch(c, "lora kernel launch");
+}
+
+he_status he_fuse_lora(he_ctx* c, const he_lora_table* t) {
+  if (!c) return HE_E_ARG;
+  if (c->failed) return set_err(c, HE_E_HIP, "context failed earlier: %s", c->err.c_str());
+  if (c->fused) return set_err(c, HE_E_STATE, "LoRA already fused");
+  he_status s = lora_common(c, t, +1.f);
+  if (s == HE_OK) c->fused = true;
+  return s;
+}
+
+he_status he_unfuse_lora(he_ctx* c, const he_lora_table* t) {
+  if (!c) return HE_E_ARG;
+  if (!c->fused) return set_err(c, HE_E_STATE, "LoRA not fused");
+  he_status s = lora_common(c, t, -1.f);
+  if (s == HE_OK) c->fused = false;
+  return s;
+}
+
+he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
+  if (!c) return HE_E_ARG;
+  if (c->failed) return set_err(c, HE_E_HIP, "context failed earlier: %s", c->err.c_str());
+  if (c->cache) return set_err(c, HE_E_STATE, "workspace already held");
+  if (max_batch < 1 || max_seq < 1) return set_err(c, HE_E_ARG, "max_batch and max_seq must be >= 1");
+  if (max_seq > c->desc.max_pos)
+    return set_err(c, HE_E_RANGE, "max_seq %d exceeds the %d learned positions", max_seq, c->desc.max_pos);
+  if (c->desc.head == HE_HEAD_LM && max_batch > kMaxDecodeBatch)
+    return set_err(c, HE_E_UNSUPPORTED, "decode batch above %d", kMaxDecodeBatch);
+  if (c->fail_next_alloc) {
+    c->fail_next_alloc = false;
+    return set_err(c, HE_E_OOM, "injected allocation failure");
+  }
+  const size_t es = esize(c->dt);
+  const int bpad = round_up(max_batch, 16);
+  const size_t rows = std::max<size_t>((size_t)max_batch * max_seq, (size_t)bpad);
+  const size_t kv_layer = (size_t)max_batch * c->H * max_seq * c->D;
+  const size_t kv_bytes = kv_layer * 2 * c->L * es;
+  // scratch layout (256-byte aligned pieces)
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
+  const size_t o_h = take(rows * c->d * 4);
+  const size_t o_x = take(rows * std::max(c->d, c->de) * es);
+  const size_t o_xe = take(c->de != c->d ? rows * c->de * es : 0);
+  const size_t o_q = take(rows * c->d * es);
+  const size_t o_o = take(rows * c->d * es);
+  const size_t o_a = take(rows * c->F * es);
+  const size_t part_elems = (size_t)bpad *
+      std::max({(size_t)c->split_qkv * 3 * c->d, (size_t)c->split_out * c->d, (size_t)c->split_fc2 * c->d});
+  const size_t o_parts = take(part_elems * 4);
+  const size_t o_logits = take((size_t)bpad * c->V * 4);
+  const size_t o_bv = take((size_t)bpad * c->n_argmax_blocks * 4);
+  const size_t o_bi = take((size_t)bpad * c->n_argmax_blocks * 4);
+  const size_t o_ids = take((size_t)bpad * 4);
+  const size_t o_tok = take((size_t)max_batch * (max_seq + 1) * 4);
+  const size_t o_pos = take(256);
+  c->max_batch = max_batch;
+  c->max_seq = max_seq;
+  c->bpad = bpad;
+  c->rows = (int)rows;
+  c->kv_layer_elems = kv_layer;
+  if (c->validate_only) {
+    c->cache = true;
+    c->prefilled = false;
+    return HE_OK;
+  }
+  void* kv = nullptr;
+  char* scratch = nullptr;
+  hipError_t e = hipMalloc(&kv, std::max<size_t>(kv_bytes, 256));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(c, HE_E_OOM, "KV cache allocation of %zu bytes failed: %s", kv_bytes, hipGetErrorString(e));
+  }
+  e = hipMalloc((void**)&scratch, off);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    hipFree(kv);
+    return set_err(c, HE_E_OOM, "scratch allocation of %zu bytes failed: %s", off, hipGetErrorString(e));
+  }
+  c->kv = kv;
+  c->scratch = scratch;
+  c->h = (float*)(scratch + o_h);
+  c->x = scratch + o_x;
+  c->xe = scratch + o_xe;
+  c->q = scratch + o_q;
+  c->o = scratch + o_o;
+  c->a = scratch + o_a;
+  c->parts = (float*)(scratch + o_parts);
+  c->logits = (float*)(scratch + o_logits);
+  c->best_val = (float*)(scratch + o_bv);
+  c->best_idx = (int32_t*)(scratch + o_bi);
+  c->ids_cur = (int32_t*)(scratch + o_ids);
+  c->tokens = (int32_t*)(scratch + o_tok);
+  c->pos_dev = (int32_t*)(scratch + o_pos);
+  c->cache = true;
+  c->prefilled = false;
+  // The decode GEMM reads X rows up to the next multiple of 16: give the padding
+  // rows defined contents once (their products are never stored).
+  HIP_TRY(c, hipMemsetAsync(c->x, 0, (size_t)bpad * std::max(c->d, c->de) * es, c->stream));
+  HIP_TRY(c, hipMemsetAsync(c->o, 0, (size_t)bpad * c->d * es, c->stream));
+  HIP_TRY(c, hipMemsetAsync(c->a, 0, (size_t)bpad * c->F * es, c->stream));
+  return HE_OK;
+}
+
+static he_status check_compute(he_ctx* c) {
+  if (c->failed) return set_err(c, HE_E_HIP, "context failed earlier: %s", c->err.c_str());
+  if (!c->cache) return set_err(c, HE_E_NOCACHE, "no workspace: call he_retake_cache");
+  return HE_OK;
+}
+
+static he_status prefill_checks(he_ctx* c, const int32_t* ids, int B, int S, const void* out) {
+  he_status s = check_compute(c);
+  if (s != HE_OK) return s;
+  if (c->desc.head != HE_HEAD_LM) return set_err(c, HE_E_UNSUPPORTED, "generation needs an LM-head model");
+  if (!ids || !out) return set_err(c, HE_E_ARG, "NULL buffer");
+  if (B < 1 || B > c->max_batch) return set_err(c, HE_E_ARG, "batch %d outside 1..%d", B, c->max_batch);
+  if (S < 1) return set_err(c, HE_E_ARG, "prompt length %d < 1", S);
+  if (S > c->max_seq) return set_err(c, HE_E_RANGE, "prompt length %d > max_seq %d", S, c->max_seq);
+  return HE_OK;
+}
+
+static he_status do_prefill(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
+  launch_set_i32(c->pos_dev, S - 1, c->stream);
+  enqueue_prefill_lm(c, ids, B, S, want_logits);
+  he_status s = check_launch(c, "prefill launch");
+  if (s != HE_OK) return s;
+  if (c->graph_B != B) drop_graphs(c);
+  c->prefilled = true;
+  c->cur_B = B;
+  c->cur_pos = S;
+  return HE_OK;
+}
+
+he_status he_prefill(he_ctx* c, const int32_t* ids, int32_t B, int32_t S, int32_t* d_next, float* d_logits) {
+  if (!c) return HE_E_ARG;
+  he_status s = prefill_checks(c, ids, B, S, d_next);
+  if (s != HE_OK) return s;
+  if (c->validate_only) {
+    c->prefilled = true; c->cur_B = B; c->cur_pos = S;
+    return HE_OK;
+  }
+  s = do_prefill(c, ids, B, S, d_logits != nullptr);
+  if (s != HE_OK) return s;
+  HIP_TRY(c, hipMemcpyAsync(d_next, c->ids_cur, (size_t)B * 4, hipMemcpyDeviceToDevice, c->stream));
+  if (d_logits)
+    HIP_TRY(c, hipMemcpyAsync(d_logits, c->logits, (size_t)B * c->V * 4, hipMemcpyDeviceToDevice, c->stream));
+  return HE_OK;
+}
+
+// One step, from the graph or launched directly.
+static he_status run_step(he_ctx* c, bool want_logits) {
+  if (c->fail_next_step) {
+    c->fail_next_step = false;
+    c->failed = true;
+    return set_err(c, HE_E_HIP, "injected device fault");
+  }
+  const int B = c->cur_B;
+  const bool graph = c->use_graph && !any_timer_armed(c);
+  if (graph) {
+    hipGraphExec_t& ge = c->graph[want_logits ? 1 : 0];
+    if (c->graph_B != B) drop_graphs(c);
+    if (!ge) {
+      hipGraph_t g = nullptr;
+      HIP_TRY(c, hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal));
+      c->capturing = true;
+      enqueue_step(c, B, want_logits, c->cur_pos);
+      c->capturing = false;
+      hipError_t e = hipStreamEndCapture(c->stream, &g);
+      if (e != hipSuccess) return hip_fail(c, e, "hipStreamEndCapture");
+      e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+      hipGraphDestroy(g);
+      if (e != hipSuccess) { ge = nullptr; return hip_fail(c, e, "hipGraphInstantiate"); }
+      c->graph_B = B;
+    }
+    HIP_TRY(c, hipGraphLaunch(ge, c->stream));
+  } else {
+    enqueue_step(c, B, want_logits, c->cur_pos);
+    he_status s = check_launch(c, "decode step launch");
+    if (s != HE_OK) return s;
+  }
+  c->cur_pos += 1;
+  return HE_OK;
+}
+
+static he_status step_checks(he_ctx* c) {
+  he_status s = check_compute(c);
+  if (s != HE_OK) return s;
+  if (!c->prefilled) return set_err(c, HE_E_STATE, "decode before a prefill in this cache epoch");
+  if (c->cur_pos >= c->max_seq)
+    return set_err(c, HE_E_RANGE, "position %d reaches max_seq %d", c->cur_pos, c->max_seq);
+  return HE_OK;
+}
+
+he_status he_decode_step(he_ctx* c, const int32_t* d_in, int32_t* d_next, float* d_logits) {
+  if (!c) return HE_E_ARG;
+  he_status s = step_checks(c);
+  if (s != HE_OK) return s;
+  if (!d_in || !d_next) return set_err(c, HE_E_ARG, "NULL buffer");
+  if (c->validate_only) {
+    if (c->fail_next_step) { c->fail_next_step = false; c->failed = true; return set_err(c, HE_E_HIP, "injected device fault"); }
+    c->cur_pos += 1;
+    return HE_OK;
+  }
+  HIP_TRY(c, hipMemcpyAsync(c->ids_cur, d_in, (size_t)c->cur_B * 4, hipMemcpyDeviceToDevice, c->stream));
+  s = run_step(c, d_logits != nullptr);
+  if (s != HE_OK) return s;
+  HIP_TRY(c, hipMemcpyAsync(d_next, c->ids_cur, (size_t)c->cur_B * 4, hipMemcpyDeviceToDevice, c->stream));
+  if (d_logits)
+    HIP_TRY(c, hipMemcpyAsync(d_logits, c->logits, (size_t)c->cur_B * c->V * 4, hipMemcpyDeviceToDevice, c->stream));
+  return HE_OK;
+}
+
+he_status he_generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g, int32_t* d_out) {
+  if (!c) return HE_E_ARG;
+  he_status s = prefill_checks(c, d_prompt, B, S, d_out);
+  if (s != HE_OK) return s;
+  if (S_g < 1) return set_err(c, HE_E_ARG, "S_g %d < 1", S_g);
+  if (S + S_g - 1 > c->max_seq)
+    return set_err(c, HE_E_RANGE, "S_p + S_g - 1 = %d exceeds max_seq %d", S + S_g - 1, c->max_seq);
+  if (c->validate_only) {
+    c->prefilled = true; c->cur_B = B; c->cur_pos = S;
+    for (int j = 1; j < S_g; ++j) {
+      if (c->fail_next_step) { c->fail_next_step = false; c->failed = true; return set_err(c, HE_E_HIP, "injected device fault"); }
+      c->cur_pos += 1;
+    }
+    return HE_OK;
+  }
+  s = do_prefill(c, d_prompt, B, S, false);
+  if (s != HE_OK) return s;
+  for (int j = 1; j < S_g; ++j) {
+    s = run_step(c, false);
+    if (s != HE_OK) return s;
+  }
+  HIP_TRY(c, hipMemcpy2DAsync(d_out, (size_t)S_g * 4, c->tokens + S, (size_t)(c->max_seq + 1) * 4,
+                              (size_t)S_g * 4, B, hipMemcpyDeviceToDevice, c->stream));
+  return HE_OK;
+}
+
+he_status he_score(he_ctx* c, const int32_t* d_ids, int32_t B, int32_t S, float* d_reward) {
+  if (!c) return HE_E_ARG;
+  he_status s = check_compute(c);
+  if (s != HE_OK) return s;
+  if (c->desc.head != HE_HEAD_SCALAR) return set_err(c, HE_E_UNSUPPORTED, "scoring needs a scalar-head model");
+  if (!d_ids || !d_reward) return set_err(c, HE_E_ARG, "NULL buffer");
+  if (B < 1 || B > c->max_batch) return set_err(c, HE_E_ARG, "batch %d outside 1..%d", B, c->max_batch);
+  if (S < 1) return set_err(c, HE_E_ARG, "length %d < 1", S);
+  if (S > c->max_seq) return set_err(c, HE_E_RANGE, "length %d > max_seq %d", S, c->max_seq);
+  if (c->validate_only) return HE_OK;
+  enqueue_score(c, d_ids, B, S, d_reward);
+  c->prefilled = false;   // the cache now holds the scored sequences
+  return check_launch(c, "score launch");
+}
+
+he_status he_sync(he_ctx* c) {
+  if (!c) return HE_E_ARG;
+  if (c->validate_only) return HE_OK;
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  HIP_TRY(c, hipGetLastError());
+  return c->failed ? HE_E_HIP : HE_OK;
+}
+
+he_status he_kernel_timer(he_ctx* c, int32_t k, int32_t enable) {
+  if (!c) return HE_E_ARG;
+  if (k < 0 || k >= HE_K_COUNT) return set_err(c, HE_E_ARG, "kernel class %d", k);
+  if (c->validate_only) return HE_OK;
+  Timer& t = c->timers[k];
+  if (!t.live.empty()) HIP_TRY(c, hipStreamSynchronize(c->stream));
+  for (auto& p : t.live) t.pool.push_back(p);
+  t.live.clear();
+  t.bytes.clear();
+  t.flops.clear();
+  t.acc = he_kernel_stat{0, 0.0, 0.0, 0.0};
+  t.armed = enable != 0;
+  return HE_OK;
+}
+
+he_status he_kernel_stats(he_ctx* c, int32_t k, he_kernel_stat* out) {
+  if (!c || !out) return HE_E_ARG;
+  if (k < 0 || k >= HE_K_COUNT) return set_err(c, HE_E_ARG, "kernel class %d", k);
+  if (c->validate_only) { *out = he_kernel_stat{0, 0.0, 0.0, 0.0}; return HE_OK; }
+  Timer& t = c->timers[k];
+  if (!t.live.empty()) HIP_TRY(c, hipStreamSynchronize(c->stream));
+  for (size_t i = 0; i < t.live.size(); ++i) {
+    float ms = 0.f;
+    HIP_TRY(c, hipEventElapsedTime(&ms, t.live[i].first, t.live[i].second));
+    t.acc.launches += 1;
+    t.acc.total_ms += ms;
+    t.acc.bytes += t.bytes[i];
+    t.acc.flops += t.flops[i];
+    t.pool.push_back(t.live[i]);
+  }
+  t.live.clear();
+  t.bytes.clear();
+  t.flops.clear();
+  *out = t.acc;
+  return HE_OK;
+}
+
+he_status he_debug(he_ctx* c, int32_t what, int64_t value) {
+  if (!c) return HE_E_ARG;
+  if (what == HE_DBG_FAIL_NEXT_ALLOC) { c->fail_next_alloc = value != 0; return HE_OK; }
+  if (what == HE_DBG_FAIL_NEXT_STEP) { c->fail_next_step = value != 0; return HE_OK; }
+  return set_err(c, HE_E_ARG, "unknown debug hook %d", what);
+}
+
+}  // extern "C"

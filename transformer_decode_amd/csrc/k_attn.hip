@@ -1,0 +1,349 @@
+// Attention kernels of libhe.
+//
+// Decode (paper summary, "Inference Mode: Generation Phase Optimizations": attention
+// specialised for one new query against a long cached context, and a KV cache to
+// which each step appends its keys and values).  One WG per (sequence, head).  The
+// WG first finishes the step's q, k, v from the projection's split-K partials
+// (fixed-order sum + bias; q scaled by D^-1/2), rounds them to the storage type and
+// appends k, v at the current position.  It then streams the cached keys and values
+// once: a group of D/8 lanes owns one key at a time (16-byte loads, a wave reads
+// whole 256-byte rows), keeps a running max / sum / weighted value sum (online
+// softmax), and the groups are merged in a fixed order through LDS.  Every K/V byte
+// is used by exactly one lane, so the loads go straight to registers.
+//
+// Prompt pass: causal attention with MFMA.  One WG per (64-query tile, sequence,
+// head); each wave owns 16 queries.  Key tiles of 64 are staged in LDS (values
+// transposed for the B operand), scores S = Q K^T and the output O += P V run on
+// v_mfma_f32_16x16x32_bf16, softmax is online per row with wave shuffles.  The
+// probabilities P enter the second product rounded to bf16.
+#include "common.h"
+#include "kernels.h"
+
+namespace he {
+
+// ---------------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restrict__ parts,
+                                                          int nsplit, const T* __restrict__ bqkv,
+                                                          T* __restrict__ kc, T* __restrict__ vc,
+                                                          const int32_t* __restrict__ pos_dev,
+                                                          T* __restrict__ o, int B, int H,
+                                                          int S_max, float q_scale) {
+  constexpr int LPK = D / 8;            // lanes per key
+  constexpr int NG = 256 / LPK;         // key groups per WG
+  __shared__ float qs[D], kn[D], vn[D];
+  __shared__ float gm[NG], gl[NG];
+  __shared__ float gacc[NG][D + 1];
+
+  const int bh = blockIdx.x, b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x;
+  const int d = H * D;
+  const int pos = *pos_dev;
+  const size_t head_base = ((size_t)b * H + h) * S_max * D;
+
+  // 1. finish q, k, v of this step and append k, v at `pos`
+  for (int i = tid; i < D; i += 256) {
+    const int c = h * D + i;
+    float q = 0.f, k = 0.f, v = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float* pr = parts + ((size_t)s * B + b) * 3 * d;
+      q += pr[c];
+      k += pr[d + c];
+      v += pr[2 * d + c];
+    }
+    q = (q + ld(bqkv + c)) * q_scale;
+    k += ld(bqkv + d + c);
+    v += ld(bqkv + 2 * d + c);
+    const T qt = to_store<T>(q), kt = to_store<T>(k), vt = to_store<T>(v);
+    kc[head_base + (size_t)pos * D + i] = kt;
+    vc[head_base + (size_t)pos * D + i] = vt;
+    qs[i] = ld(&qt);
+    kn[i] = ld(&kt);
+    vn[i] = ld(&vt);
+  }
+  __syncthreads();
+
+  // 2. stream keys 0..pos-1 from the cache; the new key (pos) comes from LDS
+  const int grp = tid / LPK, j = tid - grp * LPK;
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = qs[j * 8 + e];
+  float m_run = -INFINITY, l_run = 0.f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  auto consume = [&](float s, const float* vv) {
+    const float mn = fmaxf(m_run, s);
+    const float c = __expf(m_run - mn), p = __expf(s - mn);
+    l_run = l_run * c + p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * c + p * vv[e];
+    m_run = mn;
+  };
+  auto dot = [&](const float* kv) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(qv[e], kv[e], s);
+#pragma unroll
+    for (int off = LPK / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    return s;
+  };
+
+  const T* kb = kc + head_base + j * 8;
+  const T* vb = vc + head_base + j * 8;
+  int key = grp;
+  constexpr int U = 4;
+  for (; key + (U - 1) * NG < pos; key += U * NG) {
+    float kv[U][8], vv[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load8(kb + (size_t)(key + u * NG) * D, kv[u]);
+      load8(vb + (size_t)(key + u * NG) * D, vv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) consume(dot(kv[u]), vv[u]);
+  }
+  for (; key < pos; key += NG) {
+    float kv[8], vv[8];
+    load8(kb + (size_t)key * D, kv);
+    load8(vb + (size_t)key * D, vv);
+    consume(dot(kv), vv);
+  }
+  if (grp == pos % NG) {
+    float kv[8], vv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { kv[e] = kn[j * 8 + e]; vv[e] = vn[j * 8 + e]; }
+    consume(dot(kv), vv);
+  }
+
+  // 3. merge the groups in a fixed order
+  if (j == 0) { gm[grp] = m_run; gl[grp] = l_run; }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gacc[grp][j * 8 + e] = acc[e];
+  __syncthreads();
+  for (int i = tid; i < D; i += 256) {
+    float M = -INFINITY;
+    for (int g = 0; g < NG; ++g) M = fmaxf(M, gm[g]);
+    float L = 0.f, O = 0.f;
+    for (int g = 0; g < NG; ++g) {
+      const float w = gm[g] == -INFINITY ? 0.f : __expf(gm[g] - M);
+      L += w * gl[g];
+      O += w * gacc[g][i];
+    }
+    st(o + (size_t)b * d + h * D + i, O / L);
+  }
+}
+
+void launch_attn_decode(int dt, const float* qkv_parts, int splits, const void* b_qkv,
+                        void* k_cache, void* v_cache, const int32_t* pos_dev, void* o, int B,
+                        int H, int D, int S_max, float q_scale, hipStream_t st) {
+#define HE_DEC(T, DD)                                                                         \
+  attn_decode_kernel<T, DD><<<B * H, 256, 0, st>>>(qkv_parts, splits, (const T*)b_qkv,        \
+                                                   (T*)k_cache, (T*)v_cache, pos_dev, (T*)o, B, \
+                                                   H, S_max, q_scale)
+  if (dt == DT_BF16) {
+    switch (D) {
+      case 16: HE_DEC(bf16, 16); break;
+      case 32: HE_DEC(bf16, 32); break;
+      case 64: HE_DEC(bf16, 64); break;
+      default: HE_DEC(bf16, 128); break;
+    }
+  } else {
+    switch (D) {
+      case 16: HE_DEC(float, 16); break;
+      case 32: HE_DEC(float, 32); break;
+      case 64: HE_DEC(float, 64); break;
+      default: HE_DEC(float, 128); break;
+    }
+  }
+#undef HE_DEC
+}
+
+// ---------------------------------------------------------------------------------
+// prompt pass, bf16, MFMA
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16* __restrict__ q,
+                                                                const bf16* __restrict__ kc,
+                                                                const bf16* __restrict__ vc,
+                                                                bf16* __restrict__ o, int B,
+                                                                int S, int H, int S_max) {
+  constexpr int KT = 64;                 // keys per tile
+  constexpr int LDKS = D + 8;            // K tile row stride (bf16)
+  constexpr int LDV = KT + 8;            // transposed V row stride
+  constexpr int LDP = KT + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[KT * LDKS];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[D * LDV];
+  __shared__ __attribute__((aligned(16))) bf16 Ps[4][16 * LDP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q0 = blockIdx.x * 64;
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int d = H * D;
+  const size_t head_base = ((size_t)b * H + h) * S_max * D;
+  const int fr = lane & 15, fg = lane >> 4;
+
+  // Q fragments of this wave's 16 queries (A operand): D/32 k-steps
+  const int qrow = q0 + wv * 16 + fr;
+  bf16x8 qa[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    if (qrow < S)
+      qa[c] = *reinterpret_cast<const bf16x8*>(q + ((size_t)b * S + qrow) * d + h * D + c * 32 + fg * 8);
+    else
+      qa[c] = bf16x8{};
+  }
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_r[4], l_r[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) { m_r[r] = -INFINITY; l_r[r] = 0.f; }
+
+  const int kend = min(q0 + 64, S);
+  for (int key0 = 0; key0 < kend; key0 += KT) {
+    __syncthreads();
+    // stage K (row-major) and V (transposed) of keys key0..key0+63
+    for (int c = tid; c < KT * (D / 8); c += 256) {
+      const int kk = c / (D / 8), dc = (c - kk * (D / 8)) * 8;
+      const int key = key0 + kk;
+      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
+      if (key < S) {
+        kv4 = *reinterpret_cast<const uint4*>(kc + head_base + (size_t)key * D + dc);
+        vv4 = *reinterpret_cast<const uint4*>(vc + head_base + (size_t)key * D + dc);
+      }
+      *reinterpret_cast<uint4*>(&Ks[kk * LDKS + dc]) = kv4;
+      const bf16* vp = reinterpret_cast<const bf16*>(&vv4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(dc + e) * LDV + kk] = vp[e];
+    }
+    __syncthreads();
+
+    // scores: 16 queries x 64 keys = 4 MFMA column tiles
+    f32x4 s[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&Ks[(nt * 16 + fr) * LDKS + c * 32 + fg * 8]);
+        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], kb, s[nt], 0, 0, 0);
+      }
+    }
+    // s[nt][r] = score(query q0 + 16*wv + 4*fg + r, key key0 + 16*nt + fr)
+    float mx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qi = q0 + wv * 16 + fg * 4 + r;
+      float m = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int key = key0 + nt * 16 + fr;
+        if (key > qi || key >= S) s[nt][r] = -INFINITY;
+        m = fmaxf(m, s[nt][r]);
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      mx[r] = m;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mn = fmaxf(m_r[r], mx[r]);
+      const float c = (m_r[r] == -INFINITY) ? 0.f : __expf(m_r[r] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float p = (s[nt][r] == -INFINITY) ? 0.f : __expf(s[nt][r] - mn);
+        sum += p;
+        Ps[wv][(fg * 4 + r) * LDP + nt * 16 + fr] = f2bf(p);
+      }
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+      l_r[r] = l_r[r] * c + sum;
+      m_r[r] = mn;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) oacc[t][r] *= c;
+    }
+    __syncthreads();   // P visible to the wave's lanes
+    // O += P V over two 32-key steps
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&Ps[wv][fr * LDP + ks * 32 + fg * 8]);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&Vt[(t * 16 + fr) * LDV + ks * 32 + fg * 8]);
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc[t], 0, 0, 0);
+      }
+    }
+  }
+  // oacc[t][r] = O(query q0 + 16*wv + 4*fg + r, dim 16*t + fr)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qi = q0 + wv * 16 + fg * 4 + r;
+    if (qi >= S) continue;
+    const float inv = 1.f / l_r[r];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      o[((size_t)b * S + qi) * d + h * D + t * 16 + fr] = f2bf(oacc[t][r] * inv);
+  }
+}
+
+// fp32 models (tiny workload): one WG of 64 threads per (query, sequence, head).
+__global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __restrict__ q,
+                                                              const float* __restrict__ kc,
+                                                              const float* __restrict__ vc,
+                                                              float* __restrict__ o, int B, int S,
+                                                              int H, int D, int S_max) {
+  extern __shared__ float sm[];
+  float* qs = sm;          // [D]
+  float* sc = sm + D;      // [S]
+  const int t = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int d = H * D, tid = threadIdx.x;
+  const size_t head_base = ((size_t)b * H + h) * S_max * D;
+  for (int i = tid; i < D; i += 64) qs[i] = q[((size_t)b * S + t) * d + h * D + i];
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int key = tid; key <= t; key += 64) {
+    float s = 0.f;
+    for (int i = 0; i < D; ++i) s = fmaf(qs[i], kc[head_base + (size_t)key * D + i], s);
+    sc[key] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int key = tid; key <= t; key += 64) {
+    const float p = __expf(sc[key] - mx);
+    sc[key] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  __syncthreads();
+  for (int i = tid; i < D; i += 64) {
+    float acc = 0.f;
+    for (int key = 0; key <= t; ++key) acc = fmaf(sc[key], vc[head_base + (size_t)key * D + i], acc);
+    o[((size_t)b * S + t) * d + h * D + i] = acc / sum;
+  }
+}
+
+void launch_attn_prefill(int dt, const void* q, const void* k_cache, const void* v_cache, void* o,
+                         int B, int S, int H, int D, int S_max, hipStream_t st) {
+  if (dt == DT_BF16) {
+    dim3 grid((S + 63) / 64, B * H);
+    if (D == 64)
+      attn_prefill_bf16_kernel<64><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
+                                                         (const bf16*)v_cache, (bf16*)o, B, S, H, S_max);
+    else if (D == 128)
+      attn_prefill_bf16_kernel<128><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
+                                                          (const bf16*)v_cache, (bf16*)o, B, S, H, S_max);
+    else
+      attn_prefill_bf16_kernel<32><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
+                                                         (const bf16*)v_cache, (bf16*)o, B, S, H, S_max);
+  } else {
+    dim3 grid(S, B * H);
+    size_t lds = (size_t)(D + S) * sizeof(float);
+    attn_prefill_f32_kernel<<<grid, 64, lds, st>>>((const float*)q, (const float*)k_cache,
+                                                   (const float*)v_cache, (float*)o, B, S, H, D, S_max);
+  }
+}
+
+}  // namespace he
