@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark: Hybrid-Engine experience generation on one MI355X.
+
+One step = the generation phase of one RLHF iteration for one batch: fold the
+LoRA adapters into the actor (he_fuse_lora), greedy-generate 256 tokens for each
+256-token prompt (he_generate: prompt pass + 255 decode steps replayed from a
+hipGraph), unfold the adapters (he_unfuse_lora).  Default workload: the OPT-6.7B
+shape (32 layers, d 4096, 32 heads, FFN 16384, vocab 50272), bf16, LoRA rank 16,
+batch 64, synthetic seeded weights and prompts (pretrained weights and the
+prompt dataset are not available; the inputs have their shapes).
+
+Prints one JSON line.  value = generated tokens / s over whole steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+BF16_PEAK = 2.5e15         # MI355X dense bf16 MFMA, flop/s
+METRIC = "experience-gen tokens/s + decode HBM roofline %, OPT-6.7B-shape b64 256->256"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic(wl):
+    """Algorithmic bytes of the decode steps and flops of the prompt pass."""
+    a = wl.actor
+    L, d, F, V, B = a.n_layers, a.d_model, a.d_ffn, a.vocab, wl.batch
+    es = 2 if a.dtype == "bf16" else 4
+    layer_w = (4 * d * d + 2 * d * F) * es + (3 * d + d + F + d + 4 * d) * es   # weights, biases, LN
+    step_w = L * layer_w + V * d * es + 2 * d * es + 0 * B                        # + tied head + final LN
+    S = wl.prompt_len
+    dec_bytes = 0.0
+    dec_flops = 0.0
+    for j in range(1, wl.gen_len):
+        pos = S + j - 1                     # position fed at step j; attends over pos + 1 keys
+        kv = 2.0 * L * B * d * es * (pos + 1)   # read pos cached positions + write one
+        dec_bytes += step_w + kv
+        dec_flops += 2.0 * B * (L * (4 * d * d + 2 * d * F) + d * V) + 4.0 * L * B * d * (pos + 1)
+    pre_flops = 2.0 * B * S * L * (4 * d * d + 2 * d * F) + 2.0 * L * d * S * (S + 1) * B + 2.0 * B * d * V
+    return dec_bytes, dec_flops, pre_flops, step_w
+
+
+def cpu_baseline(wl, seed=0, layers=2, rows=(0, 1, 32, 63), steps=4):
+    """The CPU oracle on a bounded sample of the workload, extrapolated to a full row set.
+
+    Sample: the rows `rows`, the first `layers` decoder layers (LoRA fold of those
+    layers, prompt pass of 256 tokens, `steps` cached decode steps) plus the final
+    LayerNorm and LM head.  Every layer has the same shape, so the per-layer time
+    scales to all layers; decode steps scale to 255 (the per-step cost grows with
+    the context, which the sample's steps, taken at the start, understate slightly).
+    """
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import synth
+    from oracle import opt_he as O
+
+    a = wl.actor
+    rows = [r for r in rows if r < wl.batch]
+    sub = dataclasses.replace(a, n_layers=layers)
+    t0 = time.time()
+    params = synth.model_params(sub, seed)
+    lora = synth.lora_params(sub, wl.lora_rank, seed)
+    prompts = synth.prompts(wl, seed).numpy()[rows]
+    log(f"cpu baseline inputs ready in {time.time() - t0:.1f}s")
+    threads = torch.get_num_threads()
+    om = O.OracleModel(sub, params, O.Precision("bf16"), lora=lora, lora_scale=wl.lora_scale,
+                       cache_layers=True)
+    t = time.time()
+    for i in range(layers):
+        om.layer(i)                         # LoRA fold (and widening) of the sampled layers
+    t_fold = time.time() - t
+    t = time.time()
+    lg, cache = om.prefill(prompts, wl.max_seq)
+    t_prefill = time.time() - t
+    nxt = O.argmax_lowest(lg)
+    t = time.time()
+    for _ in range(steps):
+        lg = om.decode(nxt, cache)
+        nxt = O.argmax_lowest(lg)
+    t_steps = (time.time() - t) / steps
+    # the head part of one step, timed alone (it does not scale with layers)
+    h = np.zeros((len(rows), a.d_model))
+    t = time.time()
+    for _ in range(steps):
+        om.lm_logits(h)
+    t_head = (time.time() - t) / steps
+    scale = a.n_layers / layers
+    t_row_set = (t_fold * scale + (t_prefill - t_head) * scale + t_head
+                 + (wl.gen_len - 1) * ((t_steps - t_head) * scale + t_head))
+    value = len(rows) * wl.gen_len / t_row_set
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    import numpy
+    blas = "unknown"
+    try:
+        cfg = numpy.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {}).get("name", "unknown")
+    except Exception:
+        pass
+    return {
+        "value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"rows {list(rows)} of the batch, decoder layers 0..{layers - 1} of {a.n_layers} plus head: "
+                   f"LoRA fold {t_fold:.2f}s, prompt pass {t_prefill:.2f}s, {steps} decode steps "
+                   f"{t_steps:.2f}s each (head {t_head:.3f}s); extrapolated by layer count to "
+                   f"{a.n_layers} layers and by step count to {wl.gen_len - 1} steps "
+                   f"= {t_row_set:.1f}s for {len(rows)} rows x {wl.gen_len} tokens"),
+        "blas": blas, "torch_threads": threads, "precision": "float64 with bf16 storage rounding",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="opt6.7b")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-phase / per-kernel passes")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(experience generation is data parallel over prompts: run one process per GPU, "
+              f"each on its own batch)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from transformer_decode_amd import he
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    wl = synth.WORKLOADS[args.workload]
+    a = wl.actor
+    B, S, G = wl.batch, wl.prompt_len, wl.gen_len
+
+    t0 = time.time()
+    params = synth.model_params(a, args.seed)
+    lora = synth.lora_params(a, wl.lora_rank, args.seed)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    dev = {k: v.cuda() for k, v in params.items()}
+    ldev = {k: v.cuda() for k, v in lora.items()}
+    del params, lora
+    prompts = synth.prompts(wl, args.seed).cuda()
+    out = torch.empty(B, G, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"uploaded in {time.time() - t0:.1f}s")
+
+    eng = he.Engine(a, dev, use_graph=not args.no_graph)
+    ctx, st = eng.ctx, eng.stream
+    lt, _keep = eng.lora(ldev, wl.lora_rank, wl.lora_alpha)
+
+    t = time.time()
+    with torch.cuda.stream(st):
+        he.he_retake_cache(ctx, B, wl.max_seq)
+        he.he_sync(ctx)
+    t_retake = time.time() - t
+
+    def step():
+        he.he_fuse_lora(ctx, lt)
+        he.he_generate(ctx, prompts.data_ptr(), B, S, G, out.data_ptr())
+        he.he_unfuse_lora(ctx, lt)
+
+    with torch.cuda.stream(st):
+        for _ in range(args.warmup):
+            step()
+        he.he_sync(ctx)
+        log("warmup done")
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(st)
+        w0 = time.time()
+        for _ in range(args.steps):
+            step()
+        ev1.record(st)
+        he.he_sync(ctx)
+        torch.cuda.synchronize()
+        wall = time.time() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = B * G / (ms / 1e3)
+    log(f"timed {args.steps} steps: {ms:.1f} ms/step (wall {wall / args.steps * 1e3:.1f} ms/step)")
+
+    dec_bytes, dec_flops, pre_flops, step_w = algorithmic(wl)
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if a.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name}-shape actor, batch {B}, prompt {S}, generate {G} greedy, "
+                               f"LoRA rank {wl.lora_rank} fused before / unfused after",
+                   "layers": a.n_layers, "d_model": a.d_model, "heads": a.n_heads, "ffn": a.d_ffn,
+                   "vocab": a.vocab, "batch": B, "prompt_len": S, "gen_len": G,
+                   "lora_rank": wl.lora_rank, "hip_graph": not args.no_graph},
+    }
+
+    if not args.no_breakdown:
+        # per-phase times: the same step split into its calls, each bracketed by events
+        with torch.cuda.stream(st):
+            E = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+            E[0].record(st)
+            he.he_fuse_lora(ctx, lt)
+            E[1].record(st)
+            he.he_prefill(ctx, prompts.data_ptr(), B, S, nxt.data_ptr(), 0)
+            E[2].record(st)
+            for _ in range(G - 1):
+                he.he_decode_step(ctx, nxt.data_ptr(), nxt.data_ptr(), 0)
+            E[3].record(st)
+            he.he_unfuse_lora(ctx, lt)
+            E[4].record(st)
+            he.he_sync(ctx)
+            torch.cuda.synchronize()
+        t_fuse, t_pre, t_dec, t_unf = (E[i].elapsed_time(E[i + 1]) / 1e3 for i in range(4))
+        res["phases"] = {
+            "fuse_ms": t_fuse * 1e3, "prefill_ms": t_pre * 1e3, "decode_ms": t_dec * 1e3,
+            "unfuse_ms": t_unf * 1e3, "retake_ms": t_retake * 1e3,
+            "gen_tokens_per_s": B * G / (t_pre + t_dec),
+            "prefill_tokens_per_s": B * S / t_pre,
+            "decode_tokens_per_s": B * (G - 1) / t_dec,
+            "decode_hbm_GBps": dec_bytes / t_dec / 1e9,
+            "decode_hbm_frac": dec_bytes / t_dec / HBM_PEAK,
+            "prefill_TFLOPs": pre_flops / t_pre / 1e12,
+            "prefill_mfma_frac": pre_flops / t_pre / BF16_PEAK,
+            "decode_bytes_per_step_avg": dec_bytes / (G - 1),
+        }
+        log(f"phases: {json.dumps(res['phases'])}")
+
+        # per-kernel-class device time from HIP events on the library's stream
+        classes = {"attn_decode": he.HE_K_ATTN_DECODE, "gemv_decode": he.HE_K_GEMV_DECODE,
+                   "lmhead": he.HE_K_LMHEAD, "gemm_prefill": he.HE_K_GEMM_PREFILL,
+                   "attn_prefill": he.HE_K_ATTN_PREFILL, "embed_norm": he.HE_K_EMBED_NORM,
+                   "lora": he.HE_K_LORA}
+        with torch.cuda.stream(st):
+            for k in classes.values():
+                he.he_kernel_timer(ctx, k, True)
+            step()
+            he.he_sync(ctx)
+            stats = {n: he.he_kernel_stats(ctx, k) for n, k in classes.items()}
+            for k in classes.values():
+                he.he_kernel_timer(ctx, k, False)
+        kern = {}
+        for n, s in stats.items():
+            if s.launches:
+                kern[n] = {"launches": s.launches, "avg_us": s.total_ms / s.launches * 1e3,
+                           "total_ms": s.total_ms,
+                           "GBps": s.bytes / (s.total_ms / 1e3) / 1e9 if s.total_ms else None,
+                           "TFLOPs": s.flops / (s.total_ms / 1e3) / 1e12 if s.total_ms else None}
+        res["kernels"] = kern
+        dec_classes = {"attn_decode": "hbm", "gemv_decode": "hbm"}
+        dom = max(dec_classes, key=lambda n: stats[n].total_ms)
+        s = stats[dom]
+        avg_s = s.total_ms / s.launches / 1e3
+        per_launch = s.bytes / s.launches
+        res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": per_launch / avg_s / 1e9,
+                           "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                           "frac": per_launch / avg_s / HBM_PEAK, "traffic": None,
+                           "bytes_per_launch": per_launch, "avg_launch_us": avg_s * 1e6,
+                           "launches": s.launches}
+        log(f"roofline: {json.dumps(res['roofline'])}")
+
+    with torch.cuda.stream(st):
+        he.he_release_cache(ctx)
+        he.he_sync(ctx)
+    eng.close()
+
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.seed)
+        log(f"cpu baseline: {res['cpu_baseline']['value']:.2f} tokens/s")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

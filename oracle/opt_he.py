@@ -65,12 +65,24 @@ def round_bf16(x) -> np.ndarray:
     infinity.
     """
     x = np.asarray(x, dtype=np.float64)
-    _, e = np.frexp(x)
-    qe = np.maximum(e - 8, -133)
-    r = np.ldexp(np.rint(np.ldexp(x, -qe)), qe)   # np.rint: half to even
-    big = np.abs(r) >= 2.0 ** 128
-    if np.any(big):
-        r = np.where(big, np.copysign(np.inf, x), r)
+    # Normal range: float64 keeps 52 fraction bits, bfloat16 7, so round the bit
+    # pattern at bit 45, ties to even (add 2^44 - 1 plus the kept lowest bit, then
+    # clear the 45 dropped bits; a carry moves into the exponent as it should).
+    u = np.ascontiguousarray(x).view(np.uint64)
+    keep_lsb = (u >> np.uint64(45)) & np.uint64(1)
+    r = ((u + (np.uint64((1 << 44) - 1) + keep_lsb)) & ~np.uint64((1 << 45) - 1)).view(np.float64)
+    r = r.reshape(x.shape)
+    ax = np.abs(x)
+    odd = ((ax < 2.0 ** -126) & (ax > 0)) | (np.abs(r) >= 2.0 ** 128) | ~np.isfinite(x)
+    if np.any(odd):
+        xo = x[odd]
+        _, e = np.frexp(xo)
+        qe = np.maximum(e - 8, -133)
+        ro = np.ldexp(np.rint(np.ldexp(xo, -qe)), qe)   # np.rint: half to even
+        ro = np.where(np.abs(ro) >= 2.0 ** 128, np.copysign(np.inf, xo), ro)
+        ro = np.where(np.isfinite(xo), ro, xo)
+        r = r.copy()
+        r[odd] = ro
     return r
 
 

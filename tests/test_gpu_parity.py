@@ -39,6 +39,17 @@ def _fused_ref(wl, params, lora, i, key, prec):
     return O.lora_fuse(W, lora[f"lora.L{i}.{p}.A"], lora[f"lora.L{i}.{p}.B"], wl.lora_scale, prec)
 
 
+def _fused_ref_abs(wl, lora, i, key):
+    """|B| |A| for the adapters of one stored matrix (float32 error scale of the update)."""
+    def one(p):
+        A = lora[f"lora.L{i}.{p}.A"].double().abs().numpy()
+        B = lora[f"lora.L{i}.{p}.B"].double().abs().numpy()
+        return B @ A
+    if key == "qkv.w":
+        return np.concatenate([one(p) for p in ("q", "k", "v")], axis=0)
+    return one(key.split(".")[0])
+
+
 @pytest.mark.parametrize("name", ["tiny", "opt125m"])
 def test_lora_fuse_and_unfuse(name):
     wl = synth.WORKLOADS[name]
@@ -59,8 +70,14 @@ def test_lora_fuse_and_unfuse(name):
             fused_ref[i, key] = ref
             got = run.dev[f"L{i}.{key}"].double().cpu().numpy()
             if wl.actor.dtype == "bf16":
-                # one rounding of a float32-accumulated update: within one bf16 spacing
-                assert (np.abs(got - ref) <= O.ulp_bf16(ref)).all(), f"L{i}.{key} fused beyond 1 ulp"
+                # The oracle rounds W + s B A once from the exact sum; the kernel sums the
+                # rank-r update in float32 (error <= r 2^-24 s (|B| |A|)), adds it to W in
+                # float32 (2^-24 |W'|) and rounds to bf16.  So one bf16 spacing plus the
+                # float32 terms, which only matter where W and s B A nearly cancel.
+                Wabs = _fused_ref_abs(wl, lora, i, key)
+                bound = O.ulp_bf16(ref) + wl.lora_rank * 2.0 ** -24 * wl.lora_scale * Wabs \
+                    + 2.0 ** -24 * np.abs(ref)
+                assert (np.abs(got - ref) <= bound).all(), f"L{i}.{key} fused beyond the bound"
                 assert (got != ref).mean() < 1e-3, f"L{i}.{key}: too many 1-ulp differences"
             else:
                 np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
