@@ -78,7 +78,8 @@ struct he_ctx {
   int32_t* tokens = nullptr;
   int32_t* pos_dev = nullptr;
   int n_argmax_blocks = 0;
-  int split_qkv = 1, split_out = 1, split_fc2 = 1;
+  // decode GEMM plans for the current batch (set by the prompt pass)
+  GemvPlan p_qkv, p_out, p_fc1, p_fc2;
 
   // cache epoch
   bool prefilled = false;
@@ -165,12 +166,27 @@ static bool any_timer_armed(const he_ctx* c) {
   return false;
 }
 
-static int gemv_splits(int N, int K) {
-  const int nb = (N + 63) / 64;
-  const int steps = K / 32;
-  int s = (512 + nb - 1) / nb;
-  s = std::min(s, std::max(1, steps / 8));
-  return std::max(1, s);
+static void set_plans(he_ctx* c, int B) {
+  c->p_qkv = gemv_plan(B, 3 * c->d, c->d, true);
+  c->p_out = gemv_plan(B, c->d, c->d, true);
+  c->p_fc1 = gemv_plan(B, c->F, c->d, false);
+  c->p_fc2 = gemv_plan(B, c->d, c->F, true);
+}
+
+// Largest split-K partial buffer any batch size up to max_batch needs (floats).
+static size_t parts_elems(he_ctx* c, int max_batch) {
+  // the plan depends on the batch only through its multiple of 16; within one
+  // such bucket the largest batch needs the most rows
+  size_t need = 0;
+  for (int ub = 16;; ub += 16) {
+    const int B = std::min(ub, max_batch);
+    const size_t rows = (size_t)B;
+    need = std::max(need, (size_t)gemv_plan(B, 3 * c->d, c->d, true).splits * rows * 3 * c->d);
+    need = std::max(need, (size_t)gemv_plan(B, c->d, c->d, true).splits * rows * c->d);
+    need = std::max(need, (size_t)gemv_plan(B, c->d, c->F, true).splits * rows * c->d);
+    if (ub >= max_batch) break;
+  }
+  return need;
 }
 
 static void drop_graphs(he_ctx* c) {
@@ -270,30 +286,30 @@ static void enqueue_step(he_ctx* c, int B, bool want_logits, int pos) {
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
     GemvArgs gq;
-    gq.out_mode = GV_PARTIAL; gq.splits = c->split_qkv; gq.parts = c->parts;
+    gq.out_mode = GV_PARTIAL; gq.fr = c->p_qkv.fr; gq.splits = c->p_qkv.splits; gq.parts = c->parts;
     run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * es, 2.0 * B * 3 * d * d,
           [&] { launch_gemv(dt, c->x, w.w_qkv, B, 3 * d, d, gq, st); });
     run_k(c, HE_K_ATTN_DECODE, 2.0 * B * d * es * (double)(pos + 1), 4.0 * B * d * (double)(pos + 1), [&] {
-      launch_attn_decode(dt, c->parts, c->split_qkv, w.b_qkv, kcache(c, l), vcache(c, l), c->pos_dev,
+      launch_attn_decode(dt, c->parts, c->p_qkv.splits, w.b_qkv, kcache(c, l), vcache(c, l), c->pos_dev,
                          c->o, B, c->H, c->D, c->max_seq, c->q_scale, st);
     });
     GemvArgs go;
-    go.out_mode = GV_PARTIAL; go.splits = c->split_out; go.parts = c->parts;
+    go.out_mode = GV_PARTIAL; go.fr = c->p_out.fr; go.splits = c->p_out.splits; go.parts = c->parts;
     run_k(c, HE_K_GEMV_DECODE, (double)d * d * es, 2.0 * B * d * d,
           [&] { launch_gemv(dt, c->o, w.w_out, B, d, d, go, st); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
-      launch_norm(dt, c->h, c->parts, c->split_out, w.b_out, w.ln2_g, w.ln2_b, eps, c->x, B, d, 1, 0, 0, st);
+      launch_norm(dt, c->h, c->parts, c->p_out.splits, w.b_out, w.ln2_g, w.ln2_b, eps, c->x, B, d, 1, 0, 0, st);
     });
     GemvArgs g1;
-    g1.out_mode = GV_RELU; g1.bias = w.b_fc1; g1.out = c->a;
+    g1.out_mode = GV_RELU; g1.fr = c->p_fc1.fr; g1.bias = w.b_fc1; g1.out = c->a;
     run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
           [&] { launch_gemv(dt, c->x, w.w_fc1, B, F, d, g1, st); });
     GemvArgs g2;
-    g2.out_mode = GV_PARTIAL; g2.splits = c->split_fc2; g2.parts = c->parts;
+    g2.out_mode = GV_PARTIAL; g2.fr = c->p_fc2.fr; g2.splits = c->p_fc2.splits; g2.parts = c->parts;
     run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
           [&] { launch_gemv(dt, c->a, w.w_fc2, B, d, F, g2, st); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
-      launch_norm(dt, c->h, c->parts, c->split_fc2, w.b_fc2, ln_g_after(c, l), ln_b_after(c, l), eps,
+      launch_norm(dt, c->h, c->parts, c->p_fc2.splits, w.b_fc2, ln_g_after(c, l), ln_b_after(c, l), eps,
                   c->x, B, d, 1, 0, 0, st);
     });
   }
@@ -442,9 +458,6 @@ he_status he_create(const he_model_desc* desc, const he_weight_table* w, void* h
   c->validate_only = (D.flags & HE_FLAG_VALIDATE_ONLY) != 0;
   const char* ng = std::getenv("HE_NO_GRAPH");
   c->use_graph = D.use_graph && !(ng && ng[0] == '1');
-  c->split_qkv = gemv_splits(3 * c->d, c->d);
-  c->split_out = gemv_splits(c->d, c->d);
-  c->split_fc2 = gemv_splits(c->d, c->F);
   c->n_argmax_blocks = gemv_argmax_blocks(c->dt, c->V);
   if (!c->validate_only) {
     if (hip_stream) {
@@ -574,8 +587,7 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   const size_t o_q = take(rows * c->d * es);
   const size_t o_o = take(rows * c->d * es);
   const size_t o_a = take(rows * c->F * es);
-  const size_t part_elems = (size_t)bpad *
-      std::max({(size_t)c->split_qkv * 3 * c->d, (size_t)c->split_out * c->d, (size_t)c->split_fc2 * c->d});
+  const size_t part_elems = parts_elems(c, max_batch);
   const size_t o_parts = take(part_elems * 4);
   const size_t o_logits = take((size_t)bpad * c->V * 4);
   const size_t o_bv = take((size_t)bpad * c->n_argmax_blocks * 4);
@@ -649,6 +661,7 @@ static he_status prefill_checks(he_ctx* c, const int32_t* ids, int B, int S, con
 }
 
 static he_status do_prefill(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
+  set_plans(c, B);
   launch_set_i32(c->pos_dev, S - 1, c->stream);
   enqueue_prefill_lm(c, ids, B, S, want_logits);
   he_status s = check_launch(c, "prefill launch");

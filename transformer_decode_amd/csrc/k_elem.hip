@@ -12,56 +12,70 @@ namespace he {
 // bitwise-same update.  A WG owns a 32 x TK tile of W; the A and B slices it
 // needs are staged in LDS once, so HBM sees W read once and written once.
 // ---------------------------------------------------------------------------------
-constexpr int kLoraTN = 32;
-
 template <typename T, int kLoraTK>
 __global__ __launch_bounds__(256) void lora_kernel(T* __restrict__ W, const T* __restrict__ A,
                                                    const T* __restrict__ Bm, int N, int K, int r,
                                                    float s, float sign) {
+  constexpr int CPR = kLoraTK / 8;            // 8-column chunks per row
+  constexpr int RG = 256 / CPR;               // row groups, 4 rows each
+  constexpr int TN = 4 * RG;                  // rows per tile
   extern __shared__ float lds[];
-  float* As = lds;                    // [r][kLoraTK]
-  float* Bs = lds + r * kLoraTK;      // [kLoraTN][r]
-  const int k0 = blockIdx.x * kLoraTK, n0 = blockIdx.y * kLoraTN;
+  float* As = lds;                            // [r][kLoraTK]
+  float* Bs = lds + r * kLoraTK;              // [r][TN]  (transposed: 4 rows per float4)
+  const int k0 = blockIdx.x * kLoraTK, n0 = blockIdx.y * TN;
   const int tid = threadIdx.x;
+  const int c8 = tid % CPR, rg = tid / CPR;
+  const int k = k0 + c8 * 8;
+  // this thread's four rows of W, loaded before the update is formed
+  float w[4][8];
+  const bool kin = k < K;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + rg * 4 + i;
+    if (kin && n < N) load8(W + (size_t)n * K + k, w[i]);
+  }
   for (int i = tid; i < r * kLoraTK; i += 256) {
-    int j = i / kLoraTK, c = i % kLoraTK;
+    const int j = i / kLoraTK, c = i % kLoraTK;
     As[i] = (k0 + c < K) ? ld(A + (size_t)j * K + k0 + c) : 0.f;
   }
-  for (int i = tid; i < kLoraTN * r; i += 256) {
-    int n = i / r, j = i % r;
-    Bs[i] = (n0 + n < N) ? ld(Bm + (size_t)(n0 + n) * r + j) : 0.f;
+  for (int i = tid; i < TN * r; i += 256) {
+    const int n = i / r, j = i % r;
+    Bs[j * TN + n] = (n0 + n < N) ? ld(Bm + (size_t)(n0 + n) * r + j) : 0.f;
   }
   __syncthreads();
-  constexpr int CPR = kLoraTK / 8;            // 8-column chunks per row
-  constexpr int RPP = 256 / CPR;              // rows per pass
-  const int c8 = tid % CPR, sub = tid / CPR;
-  const int k = k0 + c8 * 8;
-  if (k >= K) return;
+  if (!kin) return;
+  float acc[4][8];
 #pragma unroll
-  for (int i = 0; i < kLoraTN / RPP; ++i) {
-    const int nl = sub + RPP * i, n = n0 + nl;
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
+  for (int j = 0; j < r; ++j) {
+    const float4 a0 = *reinterpret_cast<const float4*>(As + j * kLoraTK + c8 * 8);
+    const float4 a1 = *reinterpret_cast<const float4*>(As + j * kLoraTK + c8 * 8 + 4);
+    const float4 b4 = *reinterpret_cast<const float4*>(Bs + j * TN + rg * 4);
+    const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(b[i], a[q], acc[i][q]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + rg * 4 + i;
     if (n >= N) break;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < r; ++j) {
-      const float b = Bs[nl * r + j];
-      const float* a = As + j * kLoraTK + c8 * 8;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(b, a[q], acc[q]);
-    }
-    T* wp = W + (size_t)n * K + k;
-    float w[8];
-    load8(wp, w);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) w[q] = w[q] + sign * (s * acc[q]);
-    store8(wp, w);
+    for (int q = 0; q < 8; ++q) w[i][q] = w[i][q] + sign * (s * acc[i][q]);
+    store8(W + (size_t)n * K + k, w[i]);
   }
 }
 
 template <int TK>
 static void lora_launch(int dt, void* W, const void* A, const void* B, int N, int K, int r, float s,
                         float sign, hipStream_t st) {
-  dim3 grid((K + TK - 1) / TK, (N + kLoraTN - 1) / kLoraTN);
-  size_t lds = (size_t)(r * TK + kLoraTN * r) * sizeof(float);   // <= 41 KB for r <= 64
+  constexpr int TN = 4 * (256 / (TK / 8));
+  dim3 grid((K + TK - 1) / TK, (N + TN - 1) / TN);
+  size_t lds = (size_t)(r * TK + TN * r) * sizeof(float);   // <= 48 KB for r <= 64
   if (dt == DT_BF16)
     lora_kernel<bf16, TK><<<grid, 256, lds, st>>>((bf16*)W, (const bf16*)A, (const bf16*)B, N, K, r, s, sign);
   else
@@ -75,89 +89,110 @@ void launch_lora(int dt, void* W, const void* A, const void* B, int N, int K, in
 }
 
 // ---------------------------------------------------------------------------------
-// Row LayerNorm helpers: one WG of 256 threads per row, each thread owns up to
-// kMaxChunks chunks of 8 consecutive elements (d <= 8192, d % 8 == 0).  Mean and
-// biased variance are two fixed-order block reductions (deterministic).
+// Row LayerNorm: one WG per row, each thread owns up to two chunks of 4 consecutive
+// elements (d <= 8 * blockDim, d % 4 == 0).  Mean and biased variance are two
+// fixed-order block reductions (deterministic).  Wide WGs (up to 1024 threads) keep
+// many loads in flight: at decode a step has only `batch` rows.
 // ---------------------------------------------------------------------------------
-constexpr int kMaxChunks = 4;
+constexpr int kLnChunks = 2;
+
+__device__ __forceinline__ void ld4(const float* p, float* o) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+}
+__device__ __forceinline__ void ld4(const bf16* p, float* o) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
+  o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void st4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st4(bf16* p, const float* v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
 
 template <typename T>
-__device__ __forceinline__ void ln_write(const float (&v)[kMaxChunks][8], int d, float eps,
+__device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, float eps,
                                          const T* g, const T* b, T* xrow, float* hrow_post,
                                          float* red) {
-  const int tid = threadIdx.x, nch = d / 8;
+  const int tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   float s = 0.f;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    int ch = tid + c * 256;
-    if (ch < nch)
+  for (int c = 0; c < kLnChunks; ++c)
+    if (tid + c * nt < nch)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) s += v[c][q];
-  }
+      for (int q = 0; q < 4; ++q) s += v[c][q];
   const float mean = block_sum(s, red) / (float)d;
   float s2 = 0.f;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    int ch = tid + c * 256;
-    if (ch < nch)
+  for (int c = 0; c < kLnChunks; ++c)
+    if (tid + c * nt < nch)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) { float t = v[c][q] - mean; s2 += t * t; }
-  }
+      for (int q = 0; q < 4; ++q) { const float t = v[c][q] - mean; s2 += t * t; }
   const float var = block_sum(s2, red + 32) / (float)d;
   const float rstd = 1.f / sqrtf(var + eps);
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    int ch = tid + c * 256;
+  for (int c = 0; c < kLnChunks; ++c) {
+    const int ch = tid + c * nt;
     if (ch < nch) {
-      float gv[8], bv[8], y[8];
-      load8(g + ch * 8, gv);
-      load8(b + ch * 8, bv);
+      float gv[4], bv[4], y[4];
+      ld4(g + ch * 4, gv);
+      ld4(b + ch * 4, bv);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) y[q] = (v[c][q] - mean) * rstd * gv[q] + bv[q];
-      if (hrow_post) store8(hrow_post + ch * 8, y);   // post-LN: the stream is the norm
-      store8(xrow + ch * 8, y);                           // GEMM input: rounded
+      for (int q = 0; q < 4; ++q) y[q] = (v[c][q] - mean) * rstd * gv[q] + bv[q];
+      if (hrow_post) st4(hrow_post + ch * 4, y);   // post-LN: the stream is the norm
+      st4(xrow + ch * 4, y);                         // GEMM input: rounded
     }
   }
+}
+
+static int ln_threads(int d) {
+  int t = (d / 4 + 63) / 64 * 64;
+  return t < 64 ? 64 : (t > 1024 ? 1024 : t);
 }
 
 // h[m] = E[id] + P[pos + 2]; x[m] = round(LN(h[m])) (or round(h[m]) without LN).
 // Position table row pos + 2: OPT's learned positions are offset by two rows.
 template <typename T>
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* __restrict__ ids,
-                                                         const int32_t* __restrict__ pos_dev,
-                                                         int seq_len, const T* __restrict__ E,
-                                                         const T* __restrict__ P,
-                                                         const T* __restrict__ g,
-                                                         const T* __restrict__ b, float eps,
-                                                         float* __restrict__ h, T* __restrict__ x,
-                                                         int d, int vocab) {
+__global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* __restrict__ ids,
+                                                          const int32_t* __restrict__ pos_dev,
+                                                          int seq_len, const T* __restrict__ E,
+                                                          const T* __restrict__ P,
+                                                          const T* __restrict__ g,
+                                                          const T* __restrict__ b, float eps,
+                                                          float* __restrict__ h, T* __restrict__ x,
+                                                          int d, int vocab) {
   __shared__ float red[64];
-  const int m = blockIdx.x, tid = threadIdx.x, nch = d / 8;
+  const int m = blockIdx.x, tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   int id = ids[m];
   id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);   // memory safety for bad ids
   const int pos = pos_dev ? *pos_dev : (m % seq_len);
   const T* er = E + (size_t)id * d;
   const T* pr = P + (size_t)(pos + 2) * d;
-  float v[kMaxChunks][8];
+  float v[kLnChunks][4];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    int ch = tid + c * 256;
+  for (int c = 0; c < kLnChunks; ++c) {
+    const int ch = tid + c * nt;
     if (ch < nch) {
-      float e[8], p[8];
-      load8(er + ch * 8, e);
-      load8(pr + ch * 8, p);
+      float e[4], p[4];
+      ld4(er + ch * 4, e);
+      ld4(pr + ch * 4, p);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[c][q] = e[q] + p[q];
-      store8(h + (size_t)m * d + ch * 8, v[c]);
+      for (int q = 0; q < 4; ++q) v[c][q] = e[q] + p[q];
+      st4(h + (size_t)m * d + ch * 4, v[c]);
     }
   }
   if (g) {
     ln_write<T>(v, d, eps, g, b, x + (size_t)m * d, nullptr, red);
   } else {
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      int ch = tid + c * 256;
-      if (ch < nch) store8(x + (size_t)m * d + ch * 8, v[c]);
+    for (int c = 0; c < kLnChunks; ++c) {
+      const int ch = tid + c * nt;
+      if (ch < nch) st4(x + (size_t)m * d + ch * 4, v[c]);
     }
   }
 }
@@ -165,14 +200,13 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* __restri
 void launch_embed_norm(int dt, const int32_t* ids, const int32_t* pos_dev, int seq_len,
                        const void* E, const void* P, const void* g, const void* b, float eps,
                        float* h, void* x, int M, int d, int vocab, hipStream_t st) {
+  const int nt = ln_threads(d);
   if (dt == DT_BF16)
-    embed_norm_kernel<bf16><<<M, 256, 0, st>>>(ids, pos_dev, seq_len, (const bf16*)E, (const bf16*)P,
-                                               (const bf16*)g, (const bf16*)b, eps, h, (bf16*)x, d,
-                                               vocab);
+    embed_norm_kernel<bf16><<<M, nt, 0, st>>>(ids, pos_dev, seq_len, (const bf16*)E, (const bf16*)P,
+                                              (const bf16*)g, (const bf16*)b, eps, h, (bf16*)x, d, vocab);
   else
-    embed_norm_kernel<float><<<M, 256, 0, st>>>(ids, pos_dev, seq_len, (const float*)E, (const float*)P,
-                                                (const float*)g, (const float*)b, eps, h, (float*)x, d,
-                                                vocab);
+    embed_norm_kernel<float><<<M, nt, 0, st>>>(ids, pos_dev, seq_len, (const float*)E, (const float*)P,
+                                               (const float*)g, (const float*)b, eps, h, (float*)x, d, vocab);
 }
 
 template <typename T>
@@ -199,36 +233,48 @@ void launch_embed_gather(int dt, const int32_t* ids, const void* E, void* xe, in
 
 // Residual update (sum of split-K partials + bias, fixed order) and LayerNorm.
 template <typename T>
-__global__ __launch_bounds__(256) void norm_kernel(float* __restrict__ h,
-                                                   const float* __restrict__ parts, int nsplit,
-                                                   const T* __restrict__ bias,
-                                                   const T* __restrict__ g,
-                                                   const T* __restrict__ b, float eps,
-                                                   T* __restrict__ x, int M, int d, int row_stride,
-                                                   int row_offset, int post) {
+__global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
+                                                    const float* __restrict__ parts, int nsplit,
+                                                    const T* __restrict__ bias,
+                                                    const T* __restrict__ g,
+                                                    const T* __restrict__ b, float eps,
+                                                    T* __restrict__ x, int M, int d, int row_stride,
+                                                    int row_offset, int post) {
   __shared__ float red[64];
-  const int r = blockIdx.x, tid = threadIdx.x, nch = d / 8;
+  const int r = blockIdx.x, tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   const size_t row = (size_t)r * row_stride + row_offset;
   float* hr = h + row * d;
-  float v[kMaxChunks][8];
+  float v[kLnChunks][4];
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    int ch = tid + c * 256;
+  for (int c = 0; c < kLnChunks; ++c) {
+    const int ch = tid + c * nt;
     if (ch < nch) {
-      load8(hr + ch * 8, v[c]);
+      ld4(hr + ch * 4, v[c]);
       if (parts) {
-        float add[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int s = 0; s < nsplit; ++s) {
-          float pv[8];
-          load8(parts + ((size_t)s * M + r) * d + ch * 8, pv);
+        float add[4] = {0.f, 0.f, 0.f, 0.f};
+        const float* pp = parts + (size_t)r * d + ch * 4;
+        const size_t pstride = (size_t)M * d;
+        int s = 0;
+        for (; s + 4 <= nsplit; s += 4) {          // four loads in flight, summed in order
+          float p0[4], p1[4], p2[4], p3[4];
+          ld4(pp + (s + 0) * pstride, p0);
+          ld4(pp + (s + 1) * pstride, p1);
+          ld4(pp + (s + 2) * pstride, p2);
+          ld4(pp + (s + 3) * pstride, p3);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) add[q] += pv[q];
+          for (int q = 0; q < 4; ++q) add[q] = (((add[q] + p0[q]) + p1[q]) + p2[q]) + p3[q];
         }
-        float bv[8];
-        load8(bias + ch * 8, bv);
+        for (; s < nsplit; ++s) {
+          float p0[4];
+          ld4(pp + s * pstride, p0);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[c][q] += add[q] + bv[q];
-        store8(hr + ch * 8, v[c]);
+          for (int q = 0; q < 4; ++q) add[q] += p0[q];
+        }
+        float bv[4];
+        ld4(bias + ch * 4, bv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[c][q] += add[q] + bv[q];
+        st4(hr + ch * 4, v[c]);
       }
     }
   }
@@ -238,12 +284,13 @@ __global__ __launch_bounds__(256) void norm_kernel(float* __restrict__ h,
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias, const void* g,
                  const void* b, float eps, void* x, int M, int d, int row_stride, int row_offset,
                  int post, hipStream_t st) {
+  const int nt = ln_threads(d);
   if (dt == DT_BF16)
-    norm_kernel<bf16><<<M, 256, 0, st>>>(h, parts, nsplit, (const bf16*)bias, (const bf16*)g,
-                                         (const bf16*)b, eps, (bf16*)x, M, d, row_stride, row_offset, post);
+    norm_kernel<bf16><<<M, nt, 0, st>>>(h, parts, nsplit, (const bf16*)bias, (const bf16*)g,
+                                        (const bf16*)b, eps, (bf16*)x, M, d, row_stride, row_offset, post);
   else
-    norm_kernel<float><<<M, 256, 0, st>>>(h, parts, nsplit, (const float*)bias, (const float*)g,
-                                          (const float*)b, eps, (float*)x, M, d, row_stride, row_offset, post);
+    norm_kernel<float><<<M, nt, 0, st>>>(h, parts, nsplit, (const float*)bias, (const float*)g,
+                                         (const float*)b, eps, (float*)x, M, d, row_stride, row_offset, post);
 }
 
 // ---------------------------------------------------------------------------------

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace he {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
@@ -65,8 +67,18 @@ void launch_gemm(int dt, const void* X, const void* W, int M, int N, int K, cons
 // ---- decode-shaped GEMM (M = batch <= 128) ---------------------------------------
 enum GemvOut { GV_PARTIAL = 0, GV_RELU, GV_ARGMAX };
 
+// Tile/split choice for one decode projection: fr 16-row MFMA fragments per wave
+// (64 * fr rows per WG) and `splits` ways over K (partials; 1 when the epilogue
+// needs the full sum).
+struct GemvPlan {
+  int fr = 2;
+  int splits = 1;
+};
+GemvPlan gemv_plan(int M, int N, int K, bool allow_split);
+
 struct GemvArgs {
   int out_mode = GV_PARTIAL;
+  int fr = 2;                     // from gemv_plan (GV_ARGMAX always uses 2)
   int splits = 1;                 // split-K count (GV_PARTIAL only)
   float* parts = nullptr;         // GV_PARTIAL: [splits][M][N] fp32 (no bias)
   const void* bias = nullptr;     // GV_RELU
