@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-phase / per-kernel passes")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--trace-steps", type=int, default=0,
+                    help="for counter collection: run fuse + prefill + N decode steps + unfuse once, "
+                         "print nothing and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -174,6 +177,20 @@ def main():
         he.he_retake_cache(ctx, B, wl.max_seq)
         he.he_sync(ctx)
     t_retake = time.time() - t
+
+    if args.trace_steps:
+        nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+        with torch.cuda.stream(st):
+            he.he_fuse_lora(ctx, lt)
+            he.he_prefill(ctx, prompts.data_ptr(), B, S, nxt.data_ptr(), 0)
+            for _ in range(args.trace_steps):
+                he.he_decode_step(ctx, nxt.data_ptr(), nxt.data_ptr(), 0)
+            he.he_unfuse_lora(ctx, lt)
+            he.he_release_cache(ctx)
+            he.he_sync(ctx)
+        eng.close()
+        log(f"trace run done: prefill + {args.trace_steps} decode steps")
+        return
 
     def step():
         he.he_fuse_lora(ctx, lt)

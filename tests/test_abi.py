@@ -113,10 +113,24 @@ def test_state_machine_generation_cycle():
     he.he_generate(ctx, P, 2, 16, 17, P)                               # 16 + 17 - 1 = 32 fits
     assert _status(he.he_generate, ctx, P, 2, 16, 18, P) == he.HE_E_RANGE
     he.he_unfuse_lora(ctx, lt)
+    # generation runs in inference mode only (adapters folded, inference layout)
+    assert _status(he.he_prefill, ctx, P, 2, 16, P) == he.HE_E_STATE
+    assert _status(he.he_generate, ctx, P, 2, 16, 16, P) == he.HE_E_STATE
     he.he_release_cache(ctx)
     he.he_release_cache(ctx)                                           # no-op
     assert _status(he.he_decode_step, ctx, P, P) == he.HE_E_NOCACHE
     e.close()
+
+
+def test_unsupported_bf16_decode_shapes():
+    """bf16 generation models need d and d_ffn divisible by 128 and vocab by 16."""
+    import dataclasses
+    base = synth.WORKLOADS["opt125m"].actor
+    for bad in (dict(vocab=50270), dict(d_model=800, n_heads=10), dict(d_ffn=3104)):
+        shape = dataclasses.replace(base, n_layers=1, **bad)
+        with pytest.raises(he.HEError) as ei:
+            he.Engine(shape, _fake_params(shape), validate_only=True)
+        assert ei.value.status == he.HE_E_UNSUPPORTED
 
 
 def test_argument_checks():

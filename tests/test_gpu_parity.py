@@ -11,6 +11,7 @@ from oracle import opt_he as O
 from transformer_decode_amd import he
 
 from gpu_util import (GpuRun, check_logits, greedy_prefix_agrees, log, precision)
+from layout import from_inference, to_inference
 
 pytestmark = pytest.mark.gpu
 
@@ -64,11 +65,17 @@ def test_lora_fuse_and_unfuse(name):
         he.he_fuse_lora(run.ctx, lt)
         he.he_sync(run.ctx)
     fused_ref = {}
+    bf = wl.actor.dtype == "bf16"
+    if bf:   # the tied embedding (LM head weight) only changes layout
+        E0 = params["E"].double().numpy()
+        assert np.array_equal(run.dev["E"].double().cpu().numpy(), to_inference(E0))
     for i in range(wl.actor.n_layers):
         for key in keys:
             ref = _fused_ref(wl, params, lora, i, key, prec)
             fused_ref[i, key] = ref
             got = run.dev[f"L{i}.{key}"].double().cpu().numpy()
+            if bf:   # bf16 weights are held in the inference layout while fused
+                got = from_inference(got)
             if wl.actor.dtype == "bf16":
                 # The oracle rounds W + s B A once from the exact sum; the kernel sums the
                 # rank-r update in float32 (error <= r 2^-24 s (|B| |A|)), adds it to W in
@@ -84,6 +91,8 @@ def test_lora_fuse_and_unfuse(name):
     with torch.cuda.stream(run.stream):
         he.he_unfuse_lora(run.ctx, lt)
         he.he_sync(run.ctx)
+    if bf:
+        assert np.array_equal(run.dev["E"].double().cpu().numpy(), E0)
     for i in range(wl.actor.n_layers):
         for key in keys:
             W0 = params[f"L{i}.{key}"].double().numpy()

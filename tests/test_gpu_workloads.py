@@ -56,6 +56,11 @@ def test_opt6_7b_sampled_rows():
     _sampled_teacher_forced(wl, rows=[wl.batch - 1], steps=[0, 255])
 
 
+def test_opt13b_sampled_rows():
+    wl = synth.WORKLOADS["opt13b"]
+    _sampled_teacher_forced(wl, rows=[wl.batch - 1], steps=[0, 255])
+
+
 def test_two_rounds_release_retake():
     """fuse -> generate -> unfuse -> release, new adapters ("training"), retake ->
     fuse -> generate -> unfuse -> release.  Round 2 must match the oracle with the

@@ -69,6 +69,39 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------------
+// Inference layout of a bf16 weight W[N][K] (N % 16 == 0, K % 32 == 0).  W is cut into
+// blocks of 16 rows x BW columns, BW = 2^il the largest power of two <= 512 dividing
+// K.  A block keeps its place in memory (16 row segments of BW elements), but its
+// 16-byte units are reordered so that the 16 x 32 slice feeding one MFMA
+// (v_mfma_f32_16x16x32_bf16 A operand: lane l holds row l % 16, k 8 (l / 16) .. + 8)
+// is 1 KB of consecutive bytes, lane-ordered.  Unit (row j, unit column u) of a block
+// goes to position p = (u / 4) * 64 + (u % 4) * 16 + j, which is stored at block row
+// p / (BW / 8), unit column p % (BW / 8).  il == 0 means plain row-major.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ size_t il_off(int n, int k, int K, int il) {
+  if (il == 0) return (size_t)n * K + k;
+  const int bw = 1 << il, lgu = il - 3;
+  const int j = n & 15, kb = k & (bw - 1), u = kb >> 3;
+  const int p = ((u >> 2) << 6) | ((u & 3) << 4) | j;
+  return (size_t)((n & ~15) + (p >> lgu)) * K + (k - kb) + ((p & ((1 << lgu) - 1)) << 3) + (k & 7);
+}
+
+// Offset of lane l's 8 elements of MFMA fragment (row block rb, k-step s) in the
+// inference layout: rows 16 rb + l % 16, k = 32 s + 8 (l / 16) .. + 8.
+__device__ __forceinline__ size_t il_frag(int rb, int s, int lane, int K, int il) {
+  const int lgu = il - 3, fpb = 1 << (il - 5);         // units per block row, fragments per block
+  const int q = s & (fpb - 1), p = (q << 6) | lane;
+  return (size_t)(rb * 16 + (p >> lgu)) * K + ((s >> (il - 5)) << il) + ((p & ((1 << lgu) - 1)) << 3);
+}
+
+// Fragment-tiled activations X[M][K] (M <= 16 mt): the B operand of one MFMA k-step s
+// and row tile t (rows 16 t .. + 16, k 32 s .. + 32) is 1 KB at ((s * mt + t) * 512),
+// lane l holding row 16 t + l % 16, k 32 s + 8 (l / 16) .. + 8.
+__device__ __forceinline__ size_t xt_off(int m, int k, int mt) {
+  return ((size_t)((k >> 5) * mt + (m >> 4)) << 9) + (((m & 15) | (((k >> 3) & 3) << 4)) << 3) + (k & 7);
+}
+
 // Sum over the block in a fixed order (deterministic).  `red` holds >= nwaves floats.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;

@@ -3,10 +3,11 @@
 //
 // One context is one model instance (paper summary, "The DeepSpeed Hybrid Engine:
 // Architecture and Mode Switching": the engine keeps a single copy of the actor and
-// reconfigures it at the eval()/train() boundary).  Inference layout here means: the
-// LoRA adapters folded into the weights in place, and a KV workspace allocated
-// (page 2, section 3: fuse before generate, unfuse after; release the workspace
-// after generation, re-take it before the next).  The decode step can be replayed
+// reconfigures it at the eval()/train() boundary).  Inference mode here means: the
+// LoRA adapters folded into the weights in place, bf16 weights switched in the same
+// pass to the inference layout the decode kernels stream (common.h, il_off), and a
+// KV workspace allocated (page 2, section 3: fuse before generate, unfuse after;
+// release the workspace after generation, re-take it before the next).  The decode step can be replayed
 // from a captured hipGraph (page 2, section 4: enable_cuda_graph), with the step's
 // position kept in device memory so that one graph serves every step.
 #include <hip/hip_runtime.h>
@@ -56,6 +57,8 @@ struct he_ctx {
   float q_scale = 1.f;
   bool validate_only = false, use_graph = true;
   bool fused = false, failed = false;
+  // weight layout while fused: inference layout of K = d and K = F weights (bf16)
+  int il_d = 0, il_f = 0;
   std::string err;
 
   // workspace (library-owned)
@@ -77,9 +80,11 @@ struct he_ctx {
   int32_t* ids_cur = nullptr;
   int32_t* tokens = nullptr;
   int32_t* pos_dev = nullptr;
-  int n_argmax_blocks = 0;
-  // decode GEMM plans for the current batch (set by the prompt pass)
-  GemvPlan p_qkv, p_out, p_fc1, p_fc2;
+  int n_argmax_blocks = 0, argmax_cap = 0;
+  // decode GEMM plans and activation row tiles for the current batch (set by the
+  // prompt pass)
+  GemvPlan p_qkv, p_out, p_fc1, p_fc2, p_lm;
+  int xmt = 0;
 
   // cache epoch
   bool prefilled = false;
@@ -167,26 +172,40 @@ static bool any_timer_armed(const he_ctx* c) {
 }
 
 static void set_plans(he_ctx* c, int B) {
-  c->p_qkv = gemv_plan(B, 3 * c->d, c->d, true);
-  c->p_out = gemv_plan(B, c->d, c->d, true);
-  c->p_fc1 = gemv_plan(B, c->F, c->d, false);
-  c->p_fc2 = gemv_plan(B, c->d, c->F, true);
+  c->p_qkv = decode_plan(c->dt, B, 3 * c->d, c->d, true);
+  c->p_out = decode_plan(c->dt, B, c->d, c->d, true);
+  c->p_fc1 = decode_plan(c->dt, B, c->F, c->d, true);
+  c->p_fc2 = decode_plan(c->dt, B, c->d, c->F, true);
+  c->p_lm = decode_plan(c->dt, B, c->V, c->d, true, true);
+  c->xmt = c->dt == DT_BF16 ? decode_mt(B) : 0;
+  c->n_argmax_blocks = gemv_argmax_blocks(c->dt, c->p_lm, c->V);
 }
 
-// Largest split-K partial buffer any batch size up to max_batch needs (floats).
-static size_t parts_elems(he_ctx* c, int max_batch) {
-  // the plan depends on the batch only through its multiple of 16; within one
-  // such bucket the largest batch needs the most rows
+// Largest split-K partial buffer (floats) and argmax block count any batch size up
+// to max_batch needs.
+static size_t parts_elems(he_ctx* c, int max_batch, int* argmax_cap) {
   size_t need = 0;
-  for (int ub = 16;; ub += 16) {
-    const int B = std::min(ub, max_batch);
-    const size_t rows = (size_t)B;
-    need = std::max(need, (size_t)gemv_plan(B, 3 * c->d, c->d, true).splits * rows * 3 * c->d);
-    need = std::max(need, (size_t)gemv_plan(B, c->d, c->d, true).splits * rows * c->d);
-    need = std::max(need, (size_t)gemv_plan(B, c->d, c->F, true).splits * rows * c->d);
-    if (ub >= max_batch) break;
+  int nb = 0;
+  auto room = [&](const GemvPlan& p, int B, int N) { return (size_t)p.splits * (size_t)B * (size_t)N; };
+  for (int B = 1; B <= max_batch; ++B) {
+    need = std::max(need, room(decode_plan(c->dt, B, 3 * c->d, c->d, true), B, 3 * c->d));
+    need = std::max(need, room(decode_plan(c->dt, B, c->d, c->d, true), B, c->d));
+    need = std::max(need, room(decode_plan(c->dt, B, c->F, c->d, true), B, c->F));
+    need = std::max(need, room(decode_plan(c->dt, B, c->d, c->F, true), B, c->d));
+    const GemvPlan lm = decode_plan(c->dt, B, c->V, c->d, true, true);
+    need = std::max(need, room(lm, B, c->V));
+    nb = std::max(nb, gemv_argmax_blocks(c->dt, lm, c->V));
   }
+  *argmax_cap = nb;
   return need;
+}
+
+// Layout of a layer weight with K columns as the kernels must read it now.
+static int w_il(const he_ctx* c, int K) {
+  return (c->fused && c->dt == DT_BF16) ? (K == c->F ? c->il_f : c->il_d) : 0;
+}
+static int e_il(const he_ctx* c) {
+  return (c->fused && c->dt == DT_BF16 && c->desc.head == HE_HEAD_LM) ? c->il_d : 0;
 }
 
 static void drop_graphs(he_ctx* c) {
@@ -208,20 +227,57 @@ static const void* ln_b_after(he_ctx* c, int l) {
   return (l + 1 < c->L) ? c->layers[l + 1].ln1_b : c->wt.lnf_b;
 }
 
+// One decode projection into split-K partials (plan p).
+static void decode_partials(he_ctx* c, const void* X, const void* W, int B, int N, int K,
+                            const GemvPlan& p, hipStream_t st) {
+  GemvArgs g;
+  g.out_mode = GV_PARTIAL;
+  g.parts = c->parts;
+  launch_gemv(c->dt, X, W, B, N, K, p, g, st);
+}
+
+// Tied LM head over z (x rows 0..B-1) + greedy pick; advances the position counter.
+static void enqueue_lm_head(he_ctx* c, int B, bool want_logits) {
+  const int d = c->d, dt = c->dt;
+  const size_t es = esize(dt);
+  hipStream_t st = c->stream;
+  if (dt == DT_BF16 && c->p_lm.splits > 1) {
+    run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d, [&] {
+      decode_partials(c, c->x, c->wt.tok_emb, B, c->V, d, c->p_lm, st);
+      launch_reduce_argmax(c->parts, c->p_lm.splits, B, c->V, want_logits ? c->logits : nullptr,
+                           c->best_val, c->best_idx, c->n_argmax_blocks, c->pos_dev, st);
+    });
+  } else {
+    GemvArgs g;
+    g.out_mode = GV_ARGMAX;
+    g.logits = want_logits ? c->logits : nullptr;
+    g.best_val = c->best_val;
+    g.best_idx = c->best_idx;
+    g.n_blocks = c->n_argmax_blocks;
+    g.bump = c->pos_dev;
+    run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d,
+          [&] { launch_gemv(dt, c->x, c->wt.tok_emb, B, c->V, d, c->p_lm, g, st); });
+  }
+  launch_argmax_finalize(c->best_val, c->best_idx, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
+                         c->max_seq + 1, c->pos_dev, nullptr, st);
+}
+
 // Prompt pass of a pre-LN LM-head model; leaves z (final LN of the last rows) in x.
 static void enqueue_prefill_lm(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
   const int M = B * S, d = c->d, F = c->F, dt = c->dt;
   const float eps = c->desc.ln_eps;
   const size_t es = esize(dt);
   hipStream_t st = c->stream;
+  const int ild = w_il(c, d), ilf = w_il(c, F);
   run_k(c, HE_K_EMBED_NORM, (double)M * d * (2 * es + 4 + es), 0, [&] {
     launch_embed_norm(dt, ids, nullptr, S, c->wt.tok_emb, c->wt.pos_emb,
                       c->L ? c->layers[0].ln1_g : c->wt.lnf_g, c->L ? c->layers[0].ln1_b : c->wt.lnf_b,
-                      eps, c->h, c->x, M, d, c->V, st);
+                      eps, c->h, c->x, M, d, c->V, e_il(c), 0, st);
   });
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
     EpiArgs e;
+    e.w_il = ild;
     e.mode = EPI_QKV;
     e.bias = w.b_qkv;
     e.q_out = c->q;
@@ -234,41 +290,32 @@ static void enqueue_prefill_lm(he_ctx* c, const int32_t* ids, int B, int S, bool
     run_k(c, HE_K_ATTN_PREFILL, (double)M * d * es * 4, 2.0 * B * d * (double)S * (S + 1),
           [&] { launch_attn_prefill(dt, c->q, kcache(c, l), vcache(c, l), c->o, B, S, c->H, c->D, c->max_seq, st); });
     EpiArgs r;
-    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h;
+    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h; r.w_il = ild;
     run_k(c, HE_K_GEMM_PREFILL, (double)d * d * es, 2.0 * M * d * d,
           [&] { launch_gemm(dt, c->o, w.w_out, M, d, d, r, st); });
     run_k(c, HE_K_EMBED_NORM, (double)M * d * (4 + es), 0, [&] {
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, 0, st);
     });
     EpiArgs f1;
-    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a;
+    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a; f1.w_il = ild;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
           [&] { launch_gemm(dt, c->x, w.w_fc1, M, F, d, f1, st); });
     EpiArgs f2;
-    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h;
+    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h; f2.w_il = ilf;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
           [&] { launch_gemm(dt, c->a, w.w_fc2, M, d, F, f2, st); });
     if (l + 1 < c->L)
       run_k(c, HE_K_EMBED_NORM, (double)M * d * (4 + es), 0, [&] {
         launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[l + 1].ln1_g, c->layers[l + 1].ln1_b,
-                    eps, c->x, M, d, 1, 0, 0, st);
+                    eps, c->x, M, d, 1, 0, 0, 0, st);
       });
   }
-  // final LayerNorm of the last prompt position only
+  // final LayerNorm of the last prompt position only, laid out for the LM head
   run_k(c, HE_K_EMBED_NORM, (double)B * d * (4 + es), 0, [&] {
-    launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, S, S - 1, 0, st);
+    launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, S, S - 1, 0,
+                c->xmt, st);
   });
-  GemvArgs g;
-  g.out_mode = GV_ARGMAX;
-  g.logits = want_logits ? c->logits : nullptr;
-  g.best_val = c->best_val;
-  g.best_idx = c->best_idx;
-  g.n_blocks = c->n_argmax_blocks;
-  g.bump = c->pos_dev;
-  run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d,
-        [&] { launch_gemv(dt, c->x, c->wt.tok_emb, B, c->V, d, g, st); });
-  launch_argmax_finalize(c->best_val, c->best_idx, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
-                         c->max_seq + 1, c->pos_dev, nullptr, st);
+  enqueue_lm_head(c, B, want_logits);
 }
 
 // One decode step for batch B: feeds ids_cur at *pos_dev.  Host mirror `pos` is
@@ -278,56 +325,49 @@ static void enqueue_step(he_ctx* c, int B, bool want_logits, int pos) {
   const float eps = c->desc.ln_eps;
   const size_t es = esize(dt);
   hipStream_t st = c->stream;
+  const int xmt = c->xmt;
   run_k(c, HE_K_EMBED_NORM, (double)B * d * (2 * es + 4 + es), 0, [&] {
     launch_embed_norm(dt, c->ids_cur, c->pos_dev, 1, c->wt.tok_emb, c->wt.pos_emb,
                       c->L ? c->layers[0].ln1_g : c->wt.lnf_g, c->L ? c->layers[0].ln1_b : c->wt.lnf_b,
-                      eps, c->h, c->x, B, d, c->V, st);
+                      eps, c->h, c->x, B, d, c->V, e_il(c), xmt, st);
   });
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
-    GemvArgs gq;
-    gq.out_mode = GV_PARTIAL; gq.fr = c->p_qkv.fr; gq.splits = c->p_qkv.splits; gq.parts = c->parts;
     run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * es, 2.0 * B * 3 * d * d,
-          [&] { launch_gemv(dt, c->x, w.w_qkv, B, 3 * d, d, gq, st); });
+          [&] { decode_partials(c, c->x, w.w_qkv, B, 3 * d, d, c->p_qkv, st); });
     run_k(c, HE_K_ATTN_DECODE, 2.0 * B * d * es * (double)(pos + 1), 4.0 * B * d * (double)(pos + 1), [&] {
       launch_attn_decode(dt, c->parts, c->p_qkv.splits, w.b_qkv, kcache(c, l), vcache(c, l), c->pos_dev,
-                         c->o, B, c->H, c->D, c->max_seq, c->q_scale, st);
+                         c->o, B, c->H, c->D, c->max_seq, c->q_scale, xmt, st);
     });
-    GemvArgs go;
-    go.out_mode = GV_PARTIAL; go.fr = c->p_out.fr; go.splits = c->p_out.splits; go.parts = c->parts;
     run_k(c, HE_K_GEMV_DECODE, (double)d * d * es, 2.0 * B * d * d,
-          [&] { launch_gemv(dt, c->o, w.w_out, B, d, d, go, st); });
+          [&] { decode_partials(c, c->o, w.w_out, B, d, d, c->p_out, st); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
-      launch_norm(dt, c->h, c->parts, c->p_out.splits, w.b_out, w.ln2_g, w.ln2_b, eps, c->x, B, d, 1, 0, 0, st);
+      launch_norm(dt, c->h, c->parts, c->p_out.splits, w.b_out, w.ln2_g, w.ln2_b, eps, c->x, B, d, 1, 0, 0,
+                  xmt, st);
     });
-    GemvArgs g1;
-    g1.out_mode = GV_RELU; g1.fr = c->p_fc1.fr; g1.bias = w.b_fc1; g1.out = c->a;
+    if (dt == DT_BF16 && c->p_fc1.splits > 1) {
+      run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
+            [&] { decode_partials(c, c->x, w.w_fc1, B, F, d, c->p_fc1, st); });
+      run_k(c, HE_K_EMBED_NORM, (double)B * F * 4 * c->p_fc1.splits, 0,
+            [&] { launch_reduce_relu(c->parts, c->p_fc1.splits, w.b_fc1, c->a, B, F, xmt, st); });
+    } else {
+      GemvArgs g1;
+      g1.out_mode = GV_RELU; g1.bias = w.b_fc1; g1.out = c->a;
+      run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
+            [&] { launch_gemv(dt, c->x, w.w_fc1, B, F, d, c->p_fc1, g1, st); });
+    }
     run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
-          [&] { launch_gemv(dt, c->x, w.w_fc1, B, F, d, g1, st); });
-    GemvArgs g2;
-    g2.out_mode = GV_PARTIAL; g2.fr = c->p_fc2.fr; g2.splits = c->p_fc2.splits; g2.parts = c->parts;
-    run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
-          [&] { launch_gemv(dt, c->a, w.w_fc2, B, d, F, g2, st); });
+          [&] { decode_partials(c, c->a, w.w_fc2, B, d, F, c->p_fc2, st); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
       launch_norm(dt, c->h, c->parts, c->p_fc2.splits, w.b_fc2, ln_g_after(c, l), ln_b_after(c, l), eps,
-                  c->x, B, d, 1, 0, 0, st);
+                  c->x, B, d, 1, 0, 0, xmt, st);
     });
   }
   if (c->L == 0)
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
-      launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, 1, 0, 0, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, 1, 0, 0, xmt, st);
     });
-  GemvArgs g;
-  g.out_mode = GV_ARGMAX;
-  g.logits = want_logits ? c->logits : nullptr;
-  g.best_val = c->best_val;
-  g.best_idx = c->best_idx;
-  g.n_blocks = c->n_argmax_blocks;
-  g.bump = c->pos_dev;
-  run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d,
-        [&] { launch_gemv(dt, c->x, c->wt.tok_emb, B, c->V, d, g, st); });
-  launch_argmax_finalize(c->best_val, c->best_idx, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
-                         c->max_seq + 1, c->pos_dev, nullptr, st);
+  enqueue_lm_head(c, B, want_logits);
 }
 
 // Full causal pass of a scalar-head model, reward at the last position.
@@ -345,15 +385,18 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
           [&] { launch_gemm(dt, c->xe, c->wt.proj_in, M, d, de, e, st); });
     if (!post && c->L)
       launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[0].ln1_g, c->layers[0].ln1_b, eps, c->x, M, d,
-                  1, 0, 0, st);
+                  1, 0, 0, 0, st);
   } else {
     launch_embed_norm(dt, ids, nullptr, S, c->wt.tok_emb, c->wt.pos_emb,
                       (!post && c->L) ? c->layers[0].ln1_g : nullptr,
-                      (!post && c->L) ? c->layers[0].ln1_b : nullptr, eps, c->h, c->x, M, d, c->V, st);
+                      (!post && c->L) ? c->layers[0].ln1_b : nullptr, eps, c->h, c->x, M, d, c->V,
+                      e_il(c), 0, st);
   }
+  const int ild = w_il(c, d), ilf = w_il(c, F);
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
     EpiArgs e;
+    e.w_il = ild;
     e.mode = EPI_QKV; e.bias = w.b_qkv; e.q_out = c->q; e.k_cache = kcache(c, l); e.v_cache = vcache(c, l);
     e.d = d; e.H = c->H; e.D = c->D; e.S_max = c->max_seq; e.seq_len = S; e.pos0 = 0; e.q_scale = c->q_scale;
     run_k(c, HE_K_GEMM_PREFILL, (double)3 * d * d * es, 2.0 * M * 3 * d * d,
@@ -361,30 +404,30 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
     run_k(c, HE_K_ATTN_PREFILL, (double)M * d * es * 4, 2.0 * B * d * (double)S * (S + 1),
           [&] { launch_attn_prefill(dt, c->q, kcache(c, l), vcache(c, l), c->o, B, S, c->H, c->D, c->max_seq, st); });
     EpiArgs r;
-    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h;
+    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h; r.w_il = ild;
     run_k(c, HE_K_GEMM_PREFILL, (double)d * d * es, 2.0 * M * d * d,
           [&] { launch_gemm(dt, c->o, w.w_out, M, d, d, r, st); });
     if (post)
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln1_g, w.ln1_b, eps, c->x, M, d, 1, 0, 1, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln1_g, w.ln1_b, eps, c->x, M, d, 1, 0, 1, 0, st);
     else
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, 0, st);
     EpiArgs f1;
-    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a;
+    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a; f1.w_il = ild;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
           [&] { launch_gemm(dt, c->x, w.w_fc1, M, F, d, f1, st); });
     EpiArgs f2;
-    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h;
+    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h; f2.w_il = ilf;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
           [&] { launch_gemm(dt, c->a, w.w_fc2, M, d, F, f2, st); });
     if (post)
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 1, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 1, 0, st);
     else if (l + 1 < c->L)
       launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[l + 1].ln1_g, c->layers[l + 1].ln1_b, eps, c->x,
-                  M, d, 1, 0, 0, st);
+                  M, d, 1, 0, 0, 0, st);
   }
   int xs = S;
   if (!post) {   // pre-LN: final LayerNorm of the last position
-    launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, S, S - 1, 0, st);
+    launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, S, S - 1, 0, 0, st);
     xs = 1;
   }
   run_k(c, HE_K_SCORE, (double)de * d * es, 2.0 * B * de * d,
@@ -433,6 +476,9 @@ he_status he_create(const he_model_desc* desc, const he_weight_table* w, void* h
     return HE_E_UNSUPPORTED;
   if (D.d_model % 32 || D.d_ffn % 32 || de % 32 || D.d_model > 8192) return HE_E_UNSUPPORTED;
   if (D.head == HE_HEAD_LM && (D.norm != HE_NORM_PRE || de != D.d_model)) return HE_E_UNSUPPORTED;
+  // bf16 decode kernels: K ranges of 128 and 16-row weight fragments
+  if (bf && D.head == HE_HEAD_LM && (D.d_model % 128 || D.d_ffn % 128 || D.vocab % 16))
+    return HE_E_UNSUPPORTED;
   if (!w->tok_emb || !w->pos_emb || (D.n_layers > 0 && !w->layers)) return HE_E_ARG;
   if (D.norm == HE_NORM_PRE && (!w->lnf_g || !w->lnf_b)) return HE_E_ARG;
   if (de != D.d_model && (!w->proj_in || (D.head == HE_HEAD_SCALAR && !w->proj_out))) return HE_E_ARG;
@@ -455,10 +501,11 @@ he_status he_create(const he_model_desc* desc, const he_weight_table* w, void* h
   c->L = D.n_layers; c->d = D.d_model; c->H = D.n_heads; c->D = hd; c->F = D.d_ffn; c->V = D.vocab;
   c->de = de;
   c->q_scale = (float)(1.0 / std::sqrt((double)hd));
+  c->il_d = il_of(c->d);
+  c->il_f = il_of(c->F);
   c->validate_only = (D.flags & HE_FLAG_VALIDATE_ONLY) != 0;
   const char* ng = std::getenv("HE_NO_GRAPH");
   c->use_graph = D.use_graph && !(ng && ng[0] == '1');
-  c->n_argmax_blocks = gemv_argmax_blocks(c->dt, c->V);
   if (!c->validate_only) {
     if (hip_stream) {
       c->stream = (hipStream_t)hip_stream;
@@ -519,13 +566,16 @@ static he_status lora_common(he_ctx* c, const he_lora_table* t, float sign) {
       return set_err(c, HE_E_ARG, "LoRA pair %d has only one factor", i);
   if (c->validate_only) return HE_OK;
   const float s = t->alpha / (float)t->rank;
-  const int d = c->d, F = c->F, r = t->rank;
+  const int d = c->d, F = c->F;
   const size_t es = esize(c->dt);
+  // bf16: every projection changes layout (those without an adapter with r = 0)
+  const bool relayout = c->dt == DT_BF16;
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
     for (int p = 0; p < HE_N_PROJ; ++p) {
       const he_lora_pair& pr = t->pairs[l * HE_N_PROJ + p];
-      if (!pr.A) continue;
+      if (!pr.A && !relayout) continue;
+      const int r = pr.A ? t->rank : 0;
       void* W;
       int N, K;
       switch (p) {
@@ -536,10 +586,15 @@ static he_status lora_common(he_ctx* c, const he_lora_table* t, float sign) {
         case HE_PROJ_FC1: W = w.w_fc1; N = F; K = d; break;
         default: W = w.w_fc2; N = d; K = F; break;
       }
-      run_k(c, HE_K_LORA, 2.0 * N * K * es + (double)(N + K) * r * es, 2.0 * N * K * r,
-            [&] { launch_lora(c->dt, W, pr.A, pr.B, N, K, r, s, sign, c->stream); });
+      run_k(c, HE_K_LORA, 2.0 * N * K * es + (double)(N + K) * r * es, 2.0 * N * K * r, [&] {
+        launch_lora(c->dt, W, pr.A, pr.B, N, K, r, s, sign, relayout ? il_of(K) : 0, c->stream);
+      });
     }
   }
+  if (relayout && c->desc.head == HE_HEAD_LM)   // the tied embedding is the LM head's weight
+    run_k(c, HE_K_LORA, 2.0 * c->V * d * es, 0.0, [&] {
+      launch_lora(c->dt, (void*)c->wt.tok_emb, nullptr, nullptr, c->V, d, 0, 0.f, sign, c->il_d, c->stream);
+    });
   return check_launch(c, "lora kernel launch");
 }
 
@@ -574,7 +629,7 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
     return set_err(c, HE_E_OOM, "injected allocation failure");
   }
   const size_t es = esize(c->dt);
-  const int bpad = round_up(max_batch, 16);
+  const int bpad = c->dt == DT_BF16 ? 16 * decode_mt(max_batch) : round_up(max_batch, 16);
   const size_t rows = std::max<size_t>((size_t)max_batch * max_seq, (size_t)bpad);
   const size_t kv_layer = (size_t)max_batch * c->H * max_seq * c->D;
   const size_t kv_bytes = kv_layer * 2 * c->L * es;
@@ -587,17 +642,19 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   const size_t o_q = take(rows * c->d * es);
   const size_t o_o = take(rows * c->d * es);
   const size_t o_a = take(rows * c->F * es);
-  const size_t part_elems = parts_elems(c, max_batch);
+  int argmax_cap = 0;
+  const size_t part_elems = parts_elems(c, max_batch, &argmax_cap);
   const size_t o_parts = take(part_elems * 4);
   const size_t o_logits = take((size_t)bpad * c->V * 4);
-  const size_t o_bv = take((size_t)bpad * c->n_argmax_blocks * 4);
-  const size_t o_bi = take((size_t)bpad * c->n_argmax_blocks * 4);
+  const size_t o_bv = take((size_t)bpad * argmax_cap * 4);
+  const size_t o_bi = take((size_t)bpad * argmax_cap * 4);
   const size_t o_ids = take((size_t)bpad * 4);
   const size_t o_tok = take((size_t)max_batch * (max_seq + 1) * 4);
   const size_t o_pos = take(256);
   c->max_batch = max_batch;
   c->max_seq = max_seq;
   c->bpad = bpad;
+  c->argmax_cap = argmax_cap;
   c->rows = (int)rows;
   c->kv_layer_elems = kv_layer;
   if (c->validate_only) {
@@ -660,6 +717,14 @@ static he_status prefill_checks(he_ctx* c, const int32_t* ids, int B, int S, con
   return HE_OK;
 }
 
+// Generation runs in inference mode only (adapters folded, bf16 weights in the
+// inference layout); checked after the arguments.
+static he_status need_inference_mode(he_ctx* c) {
+  if (!c->fused)
+    return set_err(c, HE_E_STATE, "generation runs in inference mode: call he_fuse_lora first");
+  return HE_OK;
+}
+
 static he_status do_prefill(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
   set_plans(c, B);
   launch_set_i32(c->pos_dev, S - 1, c->stream);
@@ -676,6 +741,7 @@ static he_status do_prefill(he_ctx* c, const int32_t* ids, int B, int S, bool wa
 he_status he_prefill(he_ctx* c, const int32_t* ids, int32_t B, int32_t S, int32_t* d_next, float* d_logits) {
   if (!c) return HE_E_ARG;
   he_status s = prefill_checks(c, ids, B, S, d_next);
+  if (s == HE_OK) s = need_inference_mode(c);
   if (s != HE_OK) return s;
   if (c->validate_only) {
     c->prefilled = true; c->cur_B = B; c->cur_pos = S;
@@ -759,6 +825,8 @@ he_status he_generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, 
   if (S_g < 1) return set_err(c, HE_E_ARG, "S_g %d < 1", S_g);
   if (S + S_g - 1 > c->max_seq)
     return set_err(c, HE_E_RANGE, "S_p + S_g - 1 = %d exceeds max_seq %d", S + S_g - 1, c->max_seq);
+  s = need_inference_mode(c);
+  if (s != HE_OK) return s;
   if (c->validate_only) {
     c->prefilled = true; c->cur_B = B; c->cur_pos = S;
     for (int j = 1; j < S_g; ++j) {

@@ -15,7 +15,8 @@
 // head); each wave owns 16 queries.  Key tiles of 64 are staged in LDS (values
 // transposed for the B operand), scores S = Q K^T and the output O += P V run on
 // v_mfma_f32_16x16x32_bf16, softmax is online per row with wave shuffles.  The
-// probabilities P enter the second product rounded to bf16.
+// probabilities P enter the second product as a pair of bf16 terms (P rounded,
+// plus the rounded remainder), which keeps about 16 significant bits of P.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,13 +25,55 @@ namespace he {
 // ---------------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------------
+// Eight storage elements held as loaded (bf16 stays packed: 4 VGPRs, not 8).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void unpack(float* o) const {
+    o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
+    o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
+    o[4] = __uint_as_float(u.z << 16); o[5] = __uint_as_float(u.z & 0xffff0000u);
+    o[6] = __uint_as_float(u.w << 16); o[7] = __uint_as_float(u.w & 0xffff0000u);
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void unpack(float* o) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+// Sum over each aligned group of G lanes (G = 2, 4, 8, 16); every lane of the group
+// receives the sum.  DPP lane moves within a row of 16 lanes, no LDS traffic:
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  auto mv = [](float x, int ctrl) -> float {
+    switch (ctrl) {
+      case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+      case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+      default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    }
+  };
+  if (G >= 2) v += mv(v, 0xB1);     // quad_perm [1,0,3,2]
+  if (G >= 4) v += mv(v, 0x4E);     // quad_perm [2,3,0,1]
+  if (G >= 8) v += mv(v, 0x141);    // row_half_mirror
+  if (G >= 16) v += mv(v, 0x140);   // row_mirror
+  return v;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restrict__ parts,
+__global__ __launch_bounds__(256, (D >= 64 && sizeof(T) == 2 ? 8 : 4)) void attn_decode_kernel(const float* __restrict__ parts,
                                                           int nsplit, const T* __restrict__ bqkv,
                                                           T* __restrict__ kc, T* __restrict__ vc,
                                                           const int32_t* __restrict__ pos_dev,
                                                           T* __restrict__ o, int B, int H,
-                                                          int S_max, float q_scale) {
+                                                          int S_max, float q_scale, int x_mt) {
   constexpr int LPK = D / 8;            // lanes per key
   constexpr int NG = 256 / LPK;         // key groups per WG
   __shared__ float qs[D], kn[D], vn[D];
@@ -47,11 +90,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restric
   for (int i = tid; i < D; i += 256) {
     const int c = h * D + i;
     float q = 0.f, k = 0.f, v = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* pr = parts + ((size_t)s * B + b) * 3 * d;
-      q += pr[c];
-      k += pr[d + c];
-      v += pr[2 * d + c];
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {     // 8 splits' loads in flight, summed in order
+      float tq[8], tk[8], tv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* pr = parts + ((size_t)min(s0 + u, nsplit - 1) * B + b) * 3 * d;
+        tq[u] = pr[c];
+        tk[u] = pr[d + c];
+        tv[u] = pr[2 * d + c];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < nsplit) { q += tq[u]; k += tk[u]; v += tv[u]; }
     }
     q = (q + ld(bqkv + c)) * q_scale;
     k += ld(bqkv + d + c);
@@ -84,30 +134,46 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restric
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf(qv[e], kv[e], s);
-#pragma unroll
-    for (int off = LPK / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    return s;
+    return group_sum<LPK>(s);
   };
 
   const T* kb = kc + head_base + j * 8;
   const T* vb = vc + head_base + j * 8;
-  int key = grp;
-  constexpr int U = 4;
-  for (; key + (U - 1) * NG < pos; key += U * NG) {
-    float kv[U][8], vv[U][8];
+  // Keys 0..pos-1 in blocks of U keys per group, double buffered: block b+1 is in
+  // flight while block b is consumed.  Loads are unconditional (keys past pos-1 are
+  // clamped to pos-1 and not consumed) so every path keeps the same loads in flight.
+  constexpr int U = sizeof(T) == 2 ? 1 : 1;
+  const int nblk = (pos + U * NG - 1) / (U * NG);
+  Raw8<T> kr[2][U], vr[2][U];
+  auto load_blk = [&](int blk, Raw8<T> (&kk)[U], Raw8<T> (&vv)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      load8(kb + (size_t)(key + u * NG) * D, kv[u]);
-      load8(vb + (size_t)(key + u * NG) * D, vv[u]);
+      const int key = min(grp + NG * (blk * U + u), pos - 1);
+      kk[u].load(kb + (size_t)key * D);
+      vv[u].load(vb + (size_t)key * D);
     }
+  };
+  auto use_blk = [&](int blk, const Raw8<T> (&kk)[U], const Raw8<T> (&vv)[U]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) consume(dot(kv[u]), vv[u]);
-  }
-  for (; key < pos; key += NG) {
-    float kv[8], vv[8];
-    load8(kb + (size_t)key * D, kv);
-    load8(vb + (size_t)key * D, vv);
-    consume(dot(kv), vv);
+    for (int u = 0; u < U; ++u) {
+      const int key = grp + NG * (blk * U + u);
+      float kv[8], vx[8];
+      kk[u].unpack(kv);
+      vv[u].unpack(vx);
+      const float sc = dot(kv);           // all lanes of the group take part
+      if (key < pos) consume(sc, vx);
+    }
+  };
+  if (pos > 0) {
+    load_blk(0, kr[0], vr[0]);
+    for (int b = 0; b < nblk; b += 2) {
+      load_blk(b + 1, kr[1], vr[1]);
+      __builtin_amdgcn_sched_barrier(0);   // issue the next block before using this one
+      use_blk(b, kr[0], vr[0]);
+      load_blk(b + 2, kr[0], vr[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (b + 1 < nblk) use_blk(b + 1, kr[1], vr[1]);
+    }
   }
   if (grp == pos % NG) {
     float kv[8], vv[8];
@@ -130,18 +196,19 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restric
       L += w * gl[g];
       O += w * gacc[g][i];
     }
-    st(o + (size_t)b * d + h * D + i, O / L);
+    st(o + (x_mt ? xt_off(b, h * D + i, x_mt) : (size_t)b * d + h * D + i), O / L);
   }
 }
 
 void launch_attn_decode(int dt, const float* qkv_parts, int splits, const void* b_qkv,
                         void* k_cache, void* v_cache, const int32_t* pos_dev, void* o, int B,
-                        int H, int D, int S_max, float q_scale, hipStream_t st) {
+                        int H, int D, int S_max, float q_scale, int x_mt, hipStream_t st) {
 #define HE_DEC(T, DD)                                                                         \
   attn_decode_kernel<T, DD><<<B * H, 256, 0, st>>>(qkv_parts, splits, (const T*)b_qkv,        \
                                                    (T*)k_cache, (T*)v_cache, pos_dev, (T*)o, B, \
-                                                   H, S_max, q_scale)
+                                                   H, S_max, q_scale, XMT)
   if (dt == DT_BF16) {
+    const int XMT = x_mt;
     switch (D) {
       case 16: HE_DEC(bf16, 16); break;
       case 32: HE_DEC(bf16, 32); break;
@@ -149,6 +216,7 @@ void launch_attn_decode(int dt, const float* qkv_parts, int splits, const void* 
       default: HE_DEC(bf16, 128); break;
     }
   } else {
+    const int XMT = 0;
     switch (D) {
       case 16: HE_DEC(float, 16); break;
       case 32: HE_DEC(float, 32); break;
@@ -174,7 +242,8 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16* __re
   constexpr int LDP = KT + 8;
   __shared__ __attribute__((aligned(16))) bf16 Ks[KT * LDKS];
   __shared__ __attribute__((aligned(16))) bf16 Vt[D * LDV];
-  __shared__ __attribute__((aligned(16))) bf16 Ps[4][16 * LDP];
+  __shared__ __attribute__((aligned(16))) bf16 Ps[4][16 * LDP];     // P rounded to bf16
+  __shared__ __attribute__((aligned(16))) bf16 Pl[4][16 * LDP];     // P - round(P), rounded
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int q0 = blockIdx.x * 64;
@@ -255,7 +324,9 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16* __re
       for (int nt = 0; nt < 4; ++nt) {
         const float p = (s[nt][r] == -INFINITY) ? 0.f : __expf(s[nt][r] - mn);
         sum += p;
-        Ps[wv][(fg * 4 + r) * LDP + nt * 16 + fr] = f2bf(p);
+        const bf16 ph = f2bf(p);
+        Ps[wv][(fg * 4 + r) * LDP + nt * 16 + fr] = ph;
+        Pl[wv][(fg * 4 + r) * LDP + nt * 16 + fr] = f2bf(p - bf2f(ph));
       }
 #pragma unroll
       for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
@@ -269,10 +340,12 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16* __re
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&Ps[wv][fr * LDP + ks * 32 + fg * 8]);
+      const bf16x8 pl = *reinterpret_cast<const bf16x8*>(&Pl[wv][fr * LDP + ks * 32 + fg * 8]);
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&Vt[(t * 16 + fr) * LDV + ks * 32 + fg * 8]);
         oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, oacc[t], 0, 0, 0);
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[t], 0, 0, 0);
       }
     }
   }

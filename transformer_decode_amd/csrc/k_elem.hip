@@ -34,9 +34,12 @@ __global__ __launch_bounds__(256) void lora_kernel(T* __restrict__ W, const T* _
     const int n = n0 + rg * 4 + i;
     if (kin && n < N) load8(W + (size_t)n * K + k, w[i]);
   }
-  for (int i = tid; i < r * kLoraTK; i += 256) {
-    const int j = i / kLoraTK, c = i % kLoraTK;
-    As[i] = (k0 + c < K) ? ld(A + (size_t)j * K + k0 + c) : 0.f;
+  for (int i = tid; i < r * CPR; i += 256) {       // A slice, 16-byte chunks
+    const int j = i / CPR, c = (i % CPR) * 8;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (k0 + c < K) load8(A + (size_t)j * K + k0 + c, v);
+    *reinterpret_cast<float4*>(As + j * kLoraTK + c) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(As + j * kLoraTK + c + 4) = make_float4(v[4], v[5], v[6], v[7]);
   }
   for (int i = tid; i < TN * r; i += 256) {
     const int n = i / r, j = i % r;
@@ -71,21 +74,107 @@ __global__ __launch_bounds__(256) void lora_kernel(T* __restrict__ W, const T* _
 }
 
 template <int TK>
-static void lora_launch(int dt, void* W, const void* A, const void* B, int N, int K, int r, float s,
+static void lora_launch(void* W, const void* A, const void* B, int N, int K, int r, float s,
                         float sign, hipStream_t st) {
   constexpr int TN = 4 * (256 / (TK / 8));
   dim3 grid((K + TK - 1) / TK, (N + TN - 1) / TN);
   size_t lds = (size_t)(r * TK + TN * r) * sizeof(float);   // <= 48 KB for r <= 64
-  if (dt == DT_BF16)
-    lora_kernel<bf16, TK><<<grid, 256, lds, st>>>((bf16*)W, (const bf16*)A, (const bf16*)B, N, K, r, s, sign);
-  else
-    lora_kernel<float, TK><<<grid, 256, lds, st>>>((float*)W, (const float*)A, (const float*)B, N, K, r, s, sign);
+  lora_kernel<float, TK><<<grid, 256, lds, st>>>((float*)W, (const float*)A, (const float*)B, N, K, r, s, sign);
+}
+
+// ---------------------------------------------------------------------------------
+// bf16 models: the same fold, fused with the switch between the row-major layout
+// and the inference layout (common.h, il_off).  FOLD: read row-major, write
+// W + s B A in the inference layout; !FOLD: read the inference layout, write
+// W' - s B A row-major.  r == 0: the layout switch alone (weights without adapter).
+// A WG owns one BW-wide column block, stages A's slice once, and walks 16-row
+// blocks: each thread updates one 16-byte unit in each of four rows (the A values
+// serve all four), the block is re-ordered in LDS, then written with contiguous
+// 16-byte stores.  Each block is read completely before it is overwritten, and only
+// by its WG.  The update is accumulated exactly as in lora_kernel.
+// ---------------------------------------------------------------------------------
+template <bool FOLD>
+__global__ __launch_bounds__(256) void lora_il_kernel(bf16* __restrict__ W, const bf16* __restrict__ A,
+                                                      const bf16* __restrict__ Bm, int N, int K, int r,
+                                                      float s, float sign, int il) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  const int bw = 1 << il, upr = bw >> 3, lgu = il - 3;
+  bf16* stage = reinterpret_cast<bf16*>(lds_raw);          // [16][bw]
+  bf16* As = stage + 16 * bw;                              // [r][bw]
+  float* Bs = reinterpret_cast<float*>(As + r * bw);       // [r][16]
+  const int tid = threadIdx.x, c0 = blockIdx.x * bw, nrb = N >> 4;
+  for (int i = tid; i < r * upr; i += 256) {
+    const int j = i / upr, u = i - j * upr;
+    *reinterpret_cast<uint4*>(As + j * bw + u * 8) = *reinterpret_cast<const uint4*>(A + (size_t)j * K + c0 + u * 8);
+  }
+  for (int rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
+    __syncthreads();                                       // stage and Bs free again
+    for (int i = tid; i < 16 * r; i += 256) {
+      const int row = i / r, j = i - row * r;
+      Bs[j * 16 + row] = bf2f(Bm[(size_t)(rb * 16 + row) * r + j]);
+    }
+    __syncthreads();
+    for (int it = tid; it < 4 * upr; it += 256) {
+      const int jq = it / upr, u = it - jq * upr;          // rows 4 jq .. 4 jq + 3, unit u
+      float v[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = jq * 4 + q;
+        const int p = ((u >> 2) << 6) | ((u & 3) << 4) | j;   // inference-layout position
+        const int src = FOLD ? j * upr + u : p;
+        load8(W + (size_t)(rb * 16 + (src >> lgu)) * K + c0 + ((src & (upr - 1)) << 3), v[q]);
+      }
+      if (r > 0) {
+        float acc[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+        for (int j = 0; j < r; ++j) {
+          float a[8];
+          load8(As + j * bw + u * 8, a);
+          const float4 b4 = *reinterpret_cast<const float4*>(Bs + j * 16 + jq * 4);
+          const float b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[q][e] = fmaf(b[q], a[e], acc[q][e]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[q][e] = v[q][e] + sign * (s * acc[q][e]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = jq * 4 + q;
+        const int p = ((u >> 2) << 6) | ((u & 3) << 4) | j;
+        store8(stage + (FOLD ? p : j * upr + u) * 8, v[q]);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < 16 * upr; i += 256)
+      *reinterpret_cast<uint4*>(W + (size_t)(rb * 16 + (i >> lgu)) * K + c0 + ((i & (upr - 1)) << 3)) =
+          *reinterpret_cast<const uint4*>(stage + i * 8);
+  }
 }
 
 void launch_lora(int dt, void* W, const void* A, const void* B, int N, int K, int r, float s,
-                 float sign, hipStream_t st) {
-  if (r <= 32) lora_launch<256>(dt, W, A, B, N, K, r, s, sign, st);
-  else lora_launch<128>(dt, W, A, B, N, K, r, s, sign, st);
+                 float sign, int il, hipStream_t st) {
+  if (dt != DT_BF16) {
+    if (r <= 0) return;
+    if (r <= 32) lora_launch<256>(W, A, B, N, K, r, s, sign, st);
+    else lora_launch<128>(W, A, B, N, K, r, s, sign, st);
+    return;
+  }
+  const int bw = 1 << il, ncb = K / bw, nrb = N / 16;
+  const int gy = std::max(1, std::min(nrb, 2048 / ncb));
+  const size_t lds = (size_t)16 * bw * 2 + (size_t)r * bw * 2 + (size_t)r * 16 * 4;
+  dim3 grid(ncb, gy);
+  if (sign > 0)
+    lora_il_kernel<true><<<grid, 256, lds, st>>>((bf16*)W, (const bf16*)A, (const bf16*)B, N, K, r, s, sign, il);
+  else
+    lora_il_kernel<false><<<grid, 256, lds, st>>>((bf16*)W, (const bf16*)A, (const bf16*)B, N, K, r, s, sign, il);
 }
 
 // ---------------------------------------------------------------------------------
@@ -115,10 +204,16 @@ __device__ __forceinline__ void st4(bf16* p, const float* v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
+// x row `row` of the GEMM input: row-major [.][d], or fragment-tiled (x_mt tiles).
+template <typename T>
+__device__ __forceinline__ T* x_at(T* x, int row, int k, int d, int x_mt) {
+  return x + (x_mt ? xt_off(row, k, x_mt) : (size_t)row * d + k);
+}
+
 template <typename T>
 __device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, float eps,
-                                         const T* g, const T* b, T* xrow, float* hrow_post,
-                                         float* red) {
+                                         const T* g, const T* b, T* x, int row, int x_mt,
+                                         float* hrow_post, float* red) {
   const int tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   float s = 0.f;
 #pragma unroll
@@ -145,7 +240,7 @@ __device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, 
 #pragma unroll
       for (int q = 0; q < 4; ++q) y[q] = (v[c][q] - mean) * rstd * gv[q] + bv[q];
       if (hrow_post) st4(hrow_post + ch * 4, y);   // post-LN: the stream is the norm
-      st4(xrow + ch * 4, y);                         // GEMM input: rounded
+      st4(x_at(x, row, ch * 4, d, x_mt), y);         // GEMM input: rounded
     }
   }
 }
@@ -157,6 +252,7 @@ static int ln_threads(int d) {
 
 // h[m] = E[id] + P[pos + 2]; x[m] = round(LN(h[m])) (or round(h[m]) without LN).
 // Position table row pos + 2: OPT's learned positions are offset by two rows.
+// E may be in the inference layout (e_il > 0, it is the LM head's weight too).
 template <typename T>
 __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* __restrict__ ids,
                                                           const int32_t* __restrict__ pos_dev,
@@ -165,13 +261,12 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* __restr
                                                           const T* __restrict__ g,
                                                           const T* __restrict__ b, float eps,
                                                           float* __restrict__ h, T* __restrict__ x,
-                                                          int d, int vocab) {
+                                                          int d, int vocab, int e_il, int x_mt) {
   __shared__ float red[64];
   const int m = blockIdx.x, tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   int id = ids[m];
   id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);   // memory safety for bad ids
   const int pos = pos_dev ? *pos_dev : (m % seq_len);
-  const T* er = E + (size_t)id * d;
   const T* pr = P + (size_t)(pos + 2) * d;
   float v[kLnChunks][4];
 #pragma unroll
@@ -179,7 +274,7 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* __restr
     const int ch = tid + c * nt;
     if (ch < nch) {
       float e[4], p[4];
-      ld4(er + ch * 4, e);
+      ld4(E + il_off(id, ch * 4, d, e_il), e);
       ld4(pr + ch * 4, p);
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[c][q] = e[q] + p[q];
@@ -187,26 +282,28 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* __restr
     }
   }
   if (g) {
-    ln_write<T>(v, d, eps, g, b, x + (size_t)m * d, nullptr, red);
+    ln_write<T>(v, d, eps, g, b, x, m, x_mt, nullptr, red);
   } else {
 #pragma unroll
     for (int c = 0; c < kLnChunks; ++c) {
       const int ch = tid + c * nt;
-      if (ch < nch) st4(x + (size_t)m * d + ch * 4, v[c]);
+      if (ch < nch) st4(x_at(x, m, ch * 4, d, x_mt), v[c]);
     }
   }
 }
 
 void launch_embed_norm(int dt, const int32_t* ids, const int32_t* pos_dev, int seq_len,
                        const void* E, const void* P, const void* g, const void* b, float eps,
-                       float* h, void* x, int M, int d, int vocab, hipStream_t st) {
+                       float* h, void* x, int M, int d, int vocab, int e_il, int x_mt, hipStream_t st) {
   const int nt = ln_threads(d);
   if (dt == DT_BF16)
     embed_norm_kernel<bf16><<<M, nt, 0, st>>>(ids, pos_dev, seq_len, (const bf16*)E, (const bf16*)P,
-                                              (const bf16*)g, (const bf16*)b, eps, h, (bf16*)x, d, vocab);
+                                              (const bf16*)g, (const bf16*)b, eps, h, (bf16*)x, d, vocab,
+                                              e_il, x_mt);
   else
     embed_norm_kernel<float><<<M, nt, 0, st>>>(ids, pos_dev, seq_len, (const float*)E, (const float*)P,
-                                               (const float*)g, (const float*)b, eps, h, (float*)x, d, vocab);
+                                               (const float*)g, (const float*)b, eps, h, (float*)x, d, vocab,
+                                               0, 0);
 }
 
 template <typename T>
@@ -239,7 +336,7 @@ __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
                                                     const T* __restrict__ g,
                                                     const T* __restrict__ b, float eps,
                                                     T* __restrict__ x, int M, int d, int row_stride,
-                                                    int row_offset, int post) {
+                                                    int row_offset, int post, int x_mt) {
   __shared__ float red[64];
   const int r = blockIdx.x, tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   const size_t row = (size_t)r * row_stride + row_offset;
@@ -278,19 +375,21 @@ __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
       }
     }
   }
-  ln_write<T>(v, d, eps, g, b, x + (size_t)r * d, post ? hr : nullptr, red);
+  ln_write<T>(v, d, eps, g, b, x, r, x_mt, post ? hr : nullptr, red);
 }
 
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias, const void* g,
                  const void* b, float eps, void* x, int M, int d, int row_stride, int row_offset,
-                 int post, hipStream_t st) {
+                 int post, int x_mt, hipStream_t st) {
   const int nt = ln_threads(d);
   if (dt == DT_BF16)
     norm_kernel<bf16><<<M, nt, 0, st>>>(h, parts, nsplit, (const bf16*)bias, (const bf16*)g,
-                                        (const bf16*)b, eps, (bf16*)x, M, d, row_stride, row_offset, post);
+                                        (const bf16*)b, eps, (bf16*)x, M, d, row_stride, row_offset, post,
+                                        x_mt);
   else
     norm_kernel<float><<<M, nt, 0, st>>>(h, parts, nsplit, (const float*)bias, (const float*)g,
-                                         (const float*)b, eps, (float*)x, M, d, row_stride, row_offset, post);
+                                         (const float*)b, eps, (float*)x, M, d, row_stride, row_offset, post,
+                                         0);
 }
 
 // ---------------------------------------------------------------------------------

@@ -1,231 +1,344 @@
 // Decode-step projections of libhe: Y[M,N] = X[M,K] W[N,K]^T with M = batch <= 128.
 //
 // Generation streams every weight once per token (paper summary, "Inference Mode:
-// Generation Phase Optimizations": generation is bound by memory bandwidth; the
-// inference kernels lay weights out for sequential access).  The kernel is built
-// around that stream:
-//  * Each wave owns FR x 16 rows of W and loads them straight from HBM into the A
-//    operand of v_mfma_f32_16x16x32_bf16 with 16-byte loads (a lane holds 8
-//    consecutive k of one row; four lanes cover 64 contiguous bytes), one K-chunk
-//    ahead of the MFMAs (register double buffering).
-//  * The activation X (B rows, L2 resident) is the B operand.  The WG stages each
-//    K-chunk of X in LDS once and its four waves read it from there, so the vector
-//    memory path carries W plus only M/(64 FR) of its bytes in X.
-//  * Column blocks of 64 FR rows and an optional split over K (partials reduced
-//    later, in a fixed order, by the consuming kernel) give enough WGs to cover the
-//    256 CUs.
-// Outputs: split-K partials, bias+ReLU (rounded), or a per-block greedy argmax
-// (+ optional fp32 logits).
+// Generation Phase Optimizations": generation is bound by memory bandwidth, and the
+// inference kernels lay the weights out for sequential access).  bf16 models read W
+// in the inference layout (common.h, il_off): every 16 x 32 MFMA A operand is 1 KB
+// of consecutive bytes, so one 16-byte load per lane fetches a whole fragment with
+// fully used HBM bursts.  The activations arrive fragment-tiled too (xt_off): the B
+// operand of a k-step is 1 KB per 16 batch rows, read from L2.
+//
+//  * A wave owns FR 16-row fragments of W and a K range of kr; it keeps PD k-steps
+//    of W and X loads in flight (a register ring) ahead of its MFMAs.
+//  * The NWK waves of a WG share the rows and take consecutive K ranges; at the end
+//    they reduce through LDS in a fixed wave order, so split-K leaves K / (kr NWK)
+//    partial groups (often one) for the consumer to sum, also in a fixed order.
+//  * Epilogues: fp32 partials; bias + ReLU rounded into the next projection's tiled
+//    activations (one group only); per-WG greedy argmax (+ optional logits).
+// fp32 models (the tiny workload) use a plain FMA kernel on row-major weights.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace he {
 
-constexpr int kCS = 4;                     // 32-wide k-steps per staged chunk
-constexpr int kKC = kCS * 32;              // k per chunk
-constexpr int kLDX = kKC + 8;              // LDS row stride (bf16): 272 B, conflict-free b128 reads
+namespace {
+int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+}  // namespace
 
-int gemv_argmax_blocks(int /*dt*/, int N) { return (N + 127) / 128; }   // FR = 2 for the head
+int il_of(int K) {
+  int il = 9;
+  while (il > 5 && K % (1 << il)) --il;
+  return il;
+}
 
-// Work split of one decode projection: FR (16-row frags per wave) and K splits.
-GemvPlan gemv_plan(int M, int N, int K, bool allow_split) {
-  const int mpad = (M + 15) / 16 * 16;
-  const int steps = K / 32;
-  int smax = 1;
+int decode_mt(int M) { return pow2_ceil((M + 15) / 16); }
+
+// Work split of one decode projection.  bf16 rules, from timing every (fr, nwk, kr)
+// on the decode shapes: long K ranges win (each wave streams one long run of W; up
+// to 1024 k), then the most rows per wave (fewer activation loads per weight byte)
+// that still puts >= 512 waves in flight, then as many waves per WG (fewer partials)
+// as keeps the WG count a multiple of the 256 CUs or >= 1024.  `whole` asks for a
+// single partial group (the fused bias+ReLU and argmax epilogues).  fp32: a split
+// over K.
+GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole) {
+  GemvPlan p;
+  if (dt != DT_BF16) {
+    p.splits = allow_split ? std::max(1, std::min(K / 256, 8)) : 1;
+    return p;
+  }
+  p.mt = decode_mt(M);
+  const int nrb = N / 16, frmax = p.mt <= 4 ? 4 : 2;
+  auto choose = [&](int kr, bool need_waves) {
+    const int slices = K / kr;
+    for (int fr = frmax; fr >= 1; fr >>= 1) {
+      const long rg = (nrb + fr - 1) / fr;
+      if (need_waves && fr > 1 && rg * slices < 512) continue;
+      for (int nwk = 4; nwk >= 1; nwk >>= 1) {
+        if (slices % nwk) continue;
+        if (whole && slices != nwk) continue;
+        const long wgs = rg * (slices / nwk);
+        if (nwk > 1 && !(wgs % 256 == 0 || wgs >= 1024)) continue;
+        if (need_waves && rg * slices < 512) return false;
+        p.fr = fr; p.nwk = nwk; p.kr = kr; p.splits = slices / nwk;
+        return true;
+      }
+    }
+    return false;
+  };
+  if (whole) {   // one group: a K range of K / nwk per wave
+    for (int nwk = 1; nwk <= 4; nwk *= 2)
+      if (K % (128 * nwk) == 0 && choose(K / nwk, false)) return p;
+  }
   if (allow_split) {
-    smax = std::max(1, K / (16 * mpad));            // partial bytes <= 1/8 of weight bytes
-    smax = std::min(smax, std::max(1, steps / (2 * kCS)));
+    for (int kr = 1024; kr >= 128; kr >>= 1)
+      if (K % kr == 0 && choose(kr, true)) return p;
   }
-  GemvPlan best{2, 1};
-  long best_wg = -1;
-  for (int fr = 2; fr >= 1; --fr) {
-    const int nb = (N + 64 * fr - 1) / (64 * fr);
-    const int s = std::min(smax, std::max(1, (512 + nb - 1) / nb));
-    const long wg = (long)nb * s;
-    if (wg >= 256) return GemvPlan{fr, s};
-    if (wg > best_wg) { best_wg = wg; best = GemvPlan{fr, s}; }
-  }
-  return best;
+  // small matrices: as many waves as the shortest K range gives (K % 128 == 0 is
+  // required of bf16 models)
+  p.fr = 1; p.nwk = 1;
+  p.kr = allow_split ? 128 : K;
+  p.splits = K / p.kr;
+  return p;
+}
+
+int gemv_argmax_blocks(int dt, const GemvPlan& p, int N) {
+  if (dt == DT_BF16 && p.splits == 1) return (N / 16 + p.fr - 1) / p.fr;
+  return (N + 127) / 128;
 }
 
 __device__ __forceinline__ bool gv_better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-template <int MT, int FR>
-__device__ __forceinline__ void argmax_epilogue(const f32x4 (&acc)[FR][MT], int n_wave0, int N,
-                                                int M, const GemvArgs& g) {
-  __shared__ float sv[4][MT * 16];
-  __shared__ int si[4][MT * 16];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, grp = lane >> 4;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + (lane & 15);
-    float bv = -INFINITY;
-    int bi = min(n_wave0 + grp * 4, N - 1);
-#pragma unroll
-    for (int f = 0; f < FR; ++f)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n_wave0 + f * 16 + grp * 4 + r;
-        if (n < N) {
-          const float v = acc[f][mt][r];
-          if (g.logits && m < M) g.logits[(size_t)m * N + n] = v;
-          if (gv_better(v, n, bv, bi)) { bv = v; bi = n; }
-        }
-      }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (gv_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (grp == 0) { sv[wv][mt * 16 + (lane & 15)] = bv; si[wv][mt * 16 + (lane & 15)] = bi; }
-  }
-  __syncthreads();
-  for (int m = threadIdx.x; m < MT * 16; m += blockDim.x) {
-    float bv = sv[0][m];
-    int bi = si[0][m];
-#pragma unroll
-    for (int w = 1; w < 4; ++w)
-      if (gv_better(sv[w][m], si[w][m], bv, bi)) { bv = sv[w][m]; bi = si[w][m]; }
-    if (m < M) {
-      g.best_val[(size_t)m * g.n_blocks + blockIdx.x] = bv;
-      g.best_idx[(size_t)m * g.n_blocks + blockIdx.x] = bi;
-    }
-  }
-  if (g.bump && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *g.bump += 1;
+// Compile-time loop: f(integral_constant<0>) ... f(integral_constant<N-1>).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int MT, int FR, int OUT>
-__global__ __launch_bounds__(256) void gemv_bf16_kernel(const bf16* __restrict__ X,
-                                                        const bf16* __restrict__ W, int M, int N,
-                                                        int K, GemvArgs g) {
-  constexpr int XR = MT * 16;                 // staged X rows
-  constexpr int XCH = XR * (kKC / 8);         // 16-byte pieces per staged chunk
-  constexpr int XPT = (XCH + 255) / 256;      // pieces per thread
-  __shared__ __attribute__((aligned(16))) bf16 Xs[2][XR * kLDX];
+struct IlArgs {
+  int M, N, K, il, ns;            // ns: k-steps per wave (a multiple of 4, >= 4)
+  float* parts;                   // PARTIAL: [splits][M][N]
+  const bf16* bias;               // RELU
+  bf16* out;                      // RELU: tiled activations (mt tiles)
+  float* logits;                  // ARGMAX (nullable): [M][N]
+  float* best_val;                // ARGMAX: [M][n_blocks]
+  int32_t* best_idx;
+  int n_blocks;
+  int32_t* bump;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_wave0 = blockIdx.x * (64 * FR) + wv * 16 * FR;
-  const int ko = (lane >> 4) * 8;
-  const int steps = K / 32;
-  const int s0 = (int)((long)blockIdx.y * steps / gridDim.y);
-  const int s1 = (int)((long)(blockIdx.y + 1) * steps / gridDim.y);
-  const int nch = (s1 - s0 + kCS - 1) / kCS;
+constexpr int kPD = 3;            // k-steps of loads in flight ahead of the MFMAs
+constexpr int kNB = kPD + 1;      // ring slots
 
-  const bf16* wp[FR];
+template <int MT, int FR, int NWK, int OUT>
+__global__ __launch_bounds__(NWK * 64) void gemv_il_kernel(const bf16* __restrict__ X,
+                                                           const bf16* __restrict__ W, IlArgs a) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nrb = a.N >> 4, rb0 = blockIdx.x * FR;
+  const int s0 = (blockIdx.y * NWK + wv) * a.ns;
+  bf16x8 w[kNB][FR], x[kNB][MT];
+  int wrb[FR];
 #pragma unroll
-  for (int f = 0; f < FR; ++f)
-    wp[f] = W + (size_t)min(n_wave0 + f * 16 + (lane & 15), N - 1) * K + ko;   // clamp ragged block
-
+  for (int f = 0; f < FR; ++f) wrb[f] = min(rb0 + f, nrb - 1);
+  auto load = [&](int j, auto slot) {      // k-step s0 + j into ring slot `slot`
+    const int s = s0 + j;
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+      w[slot][f] = *reinterpret_cast<const bf16x8*>(W + il_frag(wrb[f], s, lane, a.K, a.il));
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      x[slot][t] = *reinterpret_cast<const bf16x8*>(X + ((size_t)(s * MT + t) << 9) + lane * 8);
+  };
   f32x4 acc[FR][MT];
 #pragma unroll
   for (int f = 0; f < FR; ++f)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[f][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  bf16x8 wr0[FR][kCS], wr1[FR][kCS];
-  uint4 xr[XPT];
-
-  auto load_w = [&](int c, bf16x8 (&wr)[FR][kCS]) {
+    for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](auto slot) {
 #pragma unroll
-    for (int i = 0; i < kCS; ++i) {
-      const int s = s0 + c * kCS + i;
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int f = 0; f < FR; ++f)
-        wr[f][i] = (s < s1) ? *reinterpret_cast<const bf16x8*>(wp[f] + (size_t)s * 32) : bf16x8{};
-    }
+        acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[slot][f], x[slot][t], acc[f][t], 0, 0, 0);
   };
-  auto load_x = [&](int c) {
-    const int kb = (s0 + c * kCS) * 32, ke = s1 * 32;
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int idx = tid + i * 256;
-      const int row = idx / (kKC / 8), col = (idx % (kKC / 8)) * 8;
-      xr[i] = (idx < XCH && kb + col < ke)
-                  ? *reinterpret_cast<const uint4*>(X + (size_t)row * K + kb + col)
-                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_x = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int idx = tid + i * 256;
-      if (idx < XCH) {
-        const int row = idx / (kKC / 8), col = (idx % (kKC / 8)) * 8;
-        *reinterpret_cast<uint4*>(&Xs[b][row * kLDX + col]) = xr[i];
-      }
-    }
-  };
-  auto compute = [&](int c, int b, const bf16x8 (&wr)[FR][kCS]) {
-#pragma unroll
-    for (int i = 0; i < kCS; ++i) {
-      if (s0 + c * kCS + i < s1) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 xb = *reinterpret_cast<const bf16x8*>(&Xs[b][(mt * 16 + (lane & 15)) * kLDX + i * 32 + ko]);
-#pragma unroll
-          for (int f = 0; f < FR; ++f)
-            acc[f][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wr[f][i], xb, acc[f][mt], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  load_w(0, wr0);
-  load_x(0);
-  store_x(0);
-  __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    // even chunk: compute from buffer 0 while chunk c+1 streams into buffer 1
-    if (c + 1 < nch) { load_w(c + 1, wr1); load_x(c + 1); }
-    compute(c, 0, wr0);
-    if (c + 1 < nch) store_x(1);
-    __syncthreads();
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) { load_w(c + 2, wr0); load_x(c + 2); }
-    compute(c + 1, 1, wr1);
-    if (c + 2 < nch) store_x(0);
-    __syncthreads();
+  // Steps j0 .. j0 + 3 per iteration, each issuing the loads of step j + 3 first.
+  // The last group is peeled (its single remaining load, no clamping), which keeps
+  // the ring in fixed registers and the loop's waits at "this step's loads only".
+  static_for<kPD>([&](auto i) { load(i, i); });
+  int j0 = 0;
+  for (; j0 + kNB < a.ns; j0 += kNB) {
+    static_for<kNB>([&](auto i) {
+      load(j0 + i + kPD, std::integral_constant<int, (i + kPD) % kNB>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mma(i);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
+  load(j0 + kPD, std::integral_constant<int, kPD>{});
+  static_for<kNB>([&](auto i) { mma(i); });
 
-  // acc[f][mt][r] = Y[m = mt*16 + lane%16][n = n_wave0 + 16 f + 4 (lane/16) + r]
+  // D fragment: lane holds rows n = 16 rb + 4 (lane / 16) + r of batch row 16 t + lane % 16.
+  __shared__ f32x4 red[NWK > 1 || OUT == GV_ARGMAX ? NWK : 1][FR * MT][64];
+  auto emit = [&](int f, int t, f32x4 v) {
+    const int rb = rb0 + f;
+    const int n = rb * 16 + (lane >> 4) * 4, m = t * 16 + (lane & 15);
+    if (rb >= nrb || m >= a.M) return;
+    if (OUT == GV_PARTIAL) {
+      *reinterpret_cast<f32x4*>(a.parts + ((size_t)blockIdx.y * a.M + m) * a.N + n) = v;
+    } else if (OUT == GV_RELU) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(a.bias + n);
+      const float b4[4] = {__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
+                           __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u)};
+      uint2 u;
+      u.x = (uint32_t)f2bf(fmaxf(v[0] + b4[0], 0.f)) | ((uint32_t)f2bf(fmaxf(v[1] + b4[1], 0.f)) << 16);
+      u.y = (uint32_t)f2bf(fmaxf(v[2] + b4[2], 0.f)) | ((uint32_t)f2bf(fmaxf(v[3] + b4[3], 0.f)) << 16);
+      *reinterpret_cast<uint2*>(a.out + xt_off(m, n, MT)) = u;
+    } else {
+      if (a.logits) *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.N + n) = v;
+    }
+  };
+  if (NWK > 1) {
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) red[wv][f * MT + t][lane] = acc[f][t];
+    __syncthreads();
+    for (int idx = wv; idx < FR * MT; idx += NWK) {
+      f32x4 v = red[0][idx][lane];
+#pragma unroll
+      for (int q = 1; q < NWK; ++q) v += red[q][idx][lane];
+      emit(idx / MT, idx % MT, v);
+      if (OUT == GV_ARGMAX) red[0][idx][lane] = v;   // only this wave touches slot idx of wave 0 now
+    }
+  } else {
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        emit(f, t, acc[f][t]);
+        if (OUT == GV_ARGMAX) red[0][f * MT + t][lane] = acc[f][t];
+      }
+  }
   if (OUT == GV_ARGMAX) {
-    argmax_epilogue<MT, FR>(acc, n_wave0, N, M, g);
-    return;
-  }
+    // per batch row: max over this WG's FR * 16 rows of W, lowest index on ties
+    __syncthreads();
+    for (int m = threadIdx.x; m < MT * 16; m += NWK * 64) {
+      const int t = m >> 4, c = m & 15;
+      float bv = -INFINITY;
+      int bi = min(rb0 * 16, a.N - 1);
+      for (int f = 0; f < FR && rb0 + f < nrb; ++f)
 #pragma unroll
-  for (int f = 0; f < FR; ++f) {
-    const int nb = n_wave0 + f * 16 + (lane >> 4) * 4;
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = red[0][f * MT + t][g * 16 + c];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + (lane & 15);
-      if (m >= M) continue;
-      if (OUT == GV_PARTIAL) {
-        float* dst = g.parts + ((size_t)blockIdx.y * M + m) * N + nb;
-        if (nb + 3 < N) {
-          *reinterpret_cast<float4*>(dst) = make_float4(acc[f][mt][0], acc[f][mt][1], acc[f][mt][2], acc[f][mt][3]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (nb + r < N) dst[r] = acc[f][mt][r];
-        }
-      } else {   // GV_RELU
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = nb + r;
-          if (n < N) {
-            const float v = acc[f][mt][r] + bf2f(((const bf16*)g.bias)[n]);
-            ((bf16*)g.out)[(size_t)m * N + n] = f2bf(fmaxf(v, 0.f));
+          for (int r = 0; r < 4; ++r) {
+            const int n = (rb0 + f) * 16 + g * 4 + r;
+            if (v[r] > bv) { bv = v[r]; bi = n; }     // n increases: the first maximum stays
           }
         }
+      if (m < a.M) {
+        a.best_val[(size_t)m * a.n_blocks + blockIdx.x] = bv;
+        a.best_idx[(size_t)m * a.n_blocks + blockIdx.x] = bi;
       }
     }
+    if (a.bump && blockIdx.x == 0 && threadIdx.x == 0) *a.bump += 1;
   }
 }
 
-// fp32 models: one thread per (m, n), 128 columns per WG, same output blocking.
+template <int MT, int FR, int NWK>
+static void il_launch(int out, const bf16* X, const bf16* W, const IlArgs& a, int splits,
+                      hipStream_t st) {
+  dim3 grid((a.N / 16 + FR - 1) / FR, splits);
+  if (out == GV_PARTIAL) gemv_il_kernel<MT, FR, NWK, GV_PARTIAL><<<grid, NWK * 64, 0, st>>>(X, W, a);
+  else if (out == GV_RELU) gemv_il_kernel<MT, FR, NWK, GV_RELU><<<grid, NWK * 64, 0, st>>>(X, W, a);
+  else gemv_il_kernel<MT, FR, NWK, GV_ARGMAX><<<grid, NWK * 64, 0, st>>>(X, W, a);
+}
+
+template <int MT, int FR>
+static void il_launch_nwk(int out, const bf16* X, const bf16* W, const IlArgs& a, const GemvPlan& p,
+                          hipStream_t st) {
+  if (p.nwk == 4) il_launch<MT, FR, 4>(out, X, W, a, p.splits, st);
+  else if (p.nwk == 2) il_launch<MT, FR, 2>(out, X, W, a, p.splits, st);
+  else il_launch<MT, FR, 1>(out, X, W, a, p.splits, st);
+}
+
+template <int MT>
+static void il_launch_fr(int out, const bf16* X, const bf16* W, const IlArgs& a, const GemvPlan& p,
+                         hipStream_t st) {
+  if (p.fr == 4 && MT <= 4) il_launch_nwk<MT, (MT <= 4 ? 4 : 2)>(out, X, W, a, p, st);
+  else if (p.fr >= 2) il_launch_nwk<MT, 2>(out, X, W, a, p, st);
+  else il_launch_nwk<MT, 1>(out, X, W, a, p, st);
+}
+
+// ---------------------------------------------------------------------------------
+// partial reductions
+// ---------------------------------------------------------------------------------
+// a[m][n] = round(relu(sum_s parts[s][m][n] + bias[n])), fixed order over s; written
+// fragment-tiled (mt tiles) for the next decode projection.
+__global__ __launch_bounds__(256) void reduce_relu_kernel(const float* __restrict__ parts, int S,
+                                                          const bf16* __restrict__ bias,
+                                                          bf16* __restrict__ out, int M, int N, int mt) {
+  const size_t i4 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const size_t total = (size_t)M * N;
+  if (i4 >= total) return;
+  const int n = (int)(i4 % N), m = (int)(i4 / N);
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float4 p = *reinterpret_cast<const float4*>(parts + (size_t)s * total + i4);
+    a[0] += p.x; a[1] += p.y; a[2] += p.z; a[3] += p.w;
+  }
+  uint2 u;
+  float v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = fmaxf(a[q] + bf2f(bias[n + q]), 0.f);
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(out + (mt ? xt_off(m, n, mt) : i4)) = u;
+}
+
+// logits[m][n] = sum_s parts[s][m][n]; per (m, block of 128 columns): max and its
+// lowest index -> best_val / best_idx.
+__global__ __launch_bounds__(128) void reduce_argmax_kernel(const float* __restrict__ parts, int S,
+                                                            int M, int N, float* __restrict__ logits,
+                                                            float* __restrict__ best_val,
+                                                            int32_t* __restrict__ best_idx,
+                                                            int nb, int32_t* __restrict__ bump) {
+  __shared__ float sv[2];
+  __shared__ int si[2];
+  const int m = blockIdx.y, n = blockIdx.x * 128 + threadIdx.x;
+  const size_t total = (size_t)M * N;
+  float v = -INFINITY;
+  int idx = min(blockIdx.x * 128, N - 1);
+  if (n < N) {
+    float a = 0.f;
+    for (int s = 0; s < S; ++s) a += parts[(size_t)s * total + (size_t)m * N + n];
+    if (logits) logits[(size_t)m * N + n] = a;
+    v = a;
+    idx = n;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    if (gv_better(ov, oi, v, idx)) { v = ov; idx = oi; }
+  }
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = v; si[threadIdx.x >> 6] = idx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (gv_better(sv[1], si[1], v, idx)) { v = sv[1]; idx = si[1]; }
+    best_val[(size_t)m * nb + blockIdx.x] = v;
+    best_idx[(size_t)m * nb + blockIdx.x] = idx;
+    if (bump && blockIdx.x == 0 && m == 0) *bump += 1;
+  }
+}
+
+void launch_reduce_relu(const float* parts, int S, const void* bias, void* out, int M, int N, int mt,
+                        hipStream_t st) {
+  const size_t n4 = ((size_t)M * N + 3) / 4;
+  reduce_relu_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(parts, S, (const bf16*)bias,
+                                                                  (bf16*)out, M, N, mt);
+}
+
+void launch_reduce_argmax(const float* parts, int S, int M, int N, float* logits, float* best_val,
+                          int32_t* best_idx, int nb, int32_t* bump, hipStream_t st) {
+  dim3 grid((N + 127) / 128, M);
+  reduce_argmax_kernel<<<grid, 128, 0, st>>>(parts, S, M, N, logits, best_val, best_idx, nb, bump);
+}
+
+// ---------------------------------------------------------------------------------
+// fp32 models: one thread per (m, n), 128 columns per WG, 128-column argmax blocks.
+// ---------------------------------------------------------------------------------
 template <int OUT>
 __global__ __launch_bounds__(128) void gemv_f32_kernel(const float* __restrict__ X,
                                                        const float* __restrict__ W, int M, int N,
@@ -263,40 +376,30 @@ __global__ __launch_bounds__(128) void gemv_f32_kernel(const float* __restrict__
   }
 }
 
-template <int OUT, int FR>
-static void gemv_bf16_launch(const void* X, const void* W, int M, int N, int K, const GemvArgs& g,
-                             int splits, hipStream_t st) {
-  dim3 grid((N + 64 * FR - 1) / (64 * FR), splits);
-  const int mt = (M + 15) / 16;
-  const bf16* x = (const bf16*)X;
-  const bf16* w = (const bf16*)W;
-  if (mt <= 1) gemv_bf16_kernel<1, FR, OUT><<<grid, 256, 0, st>>>(x, w, M, N, K, g);
-  else if (mt <= 2) gemv_bf16_kernel<2, FR, OUT><<<grid, 256, 0, st>>>(x, w, M, N, K, g);
-  else if (mt <= 4) gemv_bf16_kernel<4, FR, OUT><<<grid, 256, 0, st>>>(x, w, M, N, K, g);
-  else gemv_bf16_kernel<8, FR, OUT><<<grid, 256, 0, st>>>(x, w, M, N, K, g);
-}
-
-template <int OUT>
-static void gemv_dispatch(int dt, const void* X, const void* W, int M, int N, int K,
-                          const GemvArgs& g, hipStream_t st) {
+void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, const GemvPlan& p,
+                 const GemvArgs& g, hipStream_t st) {
   if (dt == DT_BF16) {
-    const int splits = OUT == GV_PARTIAL ? g.splits : 1;
-    const int fr = OUT == GV_ARGMAX ? 2 : g.fr;
-    if (fr == 2) gemv_bf16_launch<OUT, 2>(X, W, M, N, K, g, splits, st);
-    else gemv_bf16_launch<OUT, 1>(X, W, M, N, K, g, splits, st);
-  } else {
-    const int splits = OUT == GV_PARTIAL ? g.splits : 1;
-    dim3 grid((N + 127) / 128, splits, M);
-    gemv_f32_kernel<OUT><<<grid, 128, 0, st>>>((const float*)X, (const float*)W, M, N, K, g);
+    IlArgs a;
+    a.M = M; a.N = N; a.K = K; a.il = il_of(K); a.ns = p.kr / 32;
+    a.parts = g.parts; a.bias = (const bf16*)g.bias; a.out = (bf16*)g.out;
+    a.logits = g.logits; a.best_val = g.best_val; a.best_idx = g.best_idx;
+    a.n_blocks = g.n_blocks; a.bump = g.bump;
+    const bf16* x = (const bf16*)X;
+    const bf16* w = (const bf16*)W;
+    switch (p.mt) {
+      case 1: il_launch_fr<1>(g.out_mode, x, w, a, p, st); break;
+      case 2: il_launch_fr<2>(g.out_mode, x, w, a, p, st); break;
+      case 4: il_launch_fr<4>(g.out_mode, x, w, a, p, st); break;
+      default: il_launch_fr<8>(g.out_mode, x, w, a, p, st); break;
+    }
+    return;
   }
-}
-
-void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, const GemvArgs& g,
-                 hipStream_t st) {
+  const int splits = g.out_mode == GV_PARTIAL ? p.splits : 1;
+  dim3 grid((N + 127) / 128, splits, M);
   switch (g.out_mode) {
-    case GV_RELU: gemv_dispatch<GV_RELU>(dt, X, W, M, N, K, g, st); break;
-    case GV_ARGMAX: gemv_dispatch<GV_ARGMAX>(dt, X, W, M, N, K, g, st); break;
-    default: gemv_dispatch<GV_PARTIAL>(dt, X, W, M, N, K, g, st); break;
+    case GV_RELU: gemv_f32_kernel<GV_RELU><<<grid, 128, 0, st>>>((const float*)X, (const float*)W, M, N, K, g); break;
+    case GV_ARGMAX: gemv_f32_kernel<GV_ARGMAX><<<grid, 128, 0, st>>>((const float*)X, (const float*)W, M, N, K, g); break;
+    default: gemv_f32_kernel<GV_PARTIAL><<<grid, 128, 0, st>>>((const float*)X, (const float*)W, M, N, K, g); break;
   }
 }
 

@@ -10,10 +10,18 @@ namespace he {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
 
+// ---- weight layout -------------------------------------------------------------
+// Inference layout of a bf16 weight with K columns (common.h, il_off): block width
+// 2^il_of(K) (the largest power of two <= 512 dividing K).
+int il_of(int K);
+
 // ---- LoRA fold ---------------------------------------------------------------
 // W[N,K] <- round(W + sign * s * (B[N,r] A[r,K])), fixed-order fp32 accumulation.
+// fp32: in place, row-major.  bf16 (N % 16 == 0): sign > 0 reads W row-major and
+// writes the inference layout il, sign < 0 the reverse; r == 0 (A, B unused) only
+// switches the layout.
 void launch_lora(int dt, void* W, const void* A, const void* B, int N, int K, int r,
-                 float s, float sign, hipStream_t st);
+                 float s, float sign, int il, hipStream_t st);
 
 // ---- embeddings and LayerNorm ----------------------------------------------------
 // h[m] = E[id(m)] + P[pos(m) + 2] (fp32); x[m] = LN(h[m]; g, b) in storage type.
@@ -21,9 +29,12 @@ void launch_lora(int dt, void* W, const void* A, const void* B, int N, int K, in
 //   pos_dev: if non-null, every row sits at position *pos_dev (decode step);
 //            otherwise row m sits at position m % seq_len (prompt pass)
 //   g == nullptr: no LayerNorm, x[m] = round(h[m]) (post-LN models)
+//   e_il:    layout of E (0 row-major, else the inference layout)
+//   x_mt:    0: x row-major [M, d]; > 0: x fragment-tiled with x_mt row tiles (xt_off)
 void launch_embed_norm(int dt, const int32_t* ids, const int32_t* pos_dev, int seq_len,
                        const void* E, const void* P, const void* g, const void* b, float eps,
-                       float* h, void* x, int M, int d, int vocab, hipStream_t st);
+                       float* h, void* x, int M, int d, int vocab, int e_il, int x_mt,
+                       hipStream_t st);
 
 // Word-embedding gather only: xe[m] = E[ids[m]] (width de), storage type.
 void launch_embed_gather(int dt, const int32_t* ids, const void* E, void* xe, int M, int de,
@@ -35,9 +46,10 @@ void launch_embed_gather(int dt, const int32_t* ids, const void* E, void* xe, in
 //      (parts are [nsplit][M][d]; r indexes them)
 //   post == 0: x[r] = round(LN(h[row]))             (pre-LN: h untouched by the norm)
 //   post == 1: h[row] = LN(h[row]); x[r] = round(h[row])  (post-LN)
+//   x_mt > 0: x is written fragment-tiled (xt_off) for a decode projection
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias,
                  const void* g, const void* b, float eps, void* x, int M, int d,
-                 int row_stride, int row_offset, int post, hipStream_t st);
+                 int row_stride, int row_offset, int post, int x_mt, hipStream_t st);
 
 // ---- GEMM epilogues ------------------------------------------------------------
 enum Epi { EPI_QKV = 0, EPI_RESID, EPI_RELU, EPI_POSADD, EPI_F32 };
@@ -58,6 +70,8 @@ struct EpiArgs {
   void* out = nullptr;            // [M, N] storage type
   // EPI_F32
   float* out_f32 = nullptr;       // [M, N]
+  // layout of the bf16 weight W: 0 row-major, else the inference layout (il_off)
+  int w_il = 0;
 };
 
 // Y[M,N] = X[M,K] W[N,K]^T with the epilogue (prompt-pass shapes, M large).
@@ -67,34 +81,47 @@ void launch_gemm(int dt, const void* X, const void* W, int M, int N, int K, cons
 // ---- decode-shaped GEMM (M = batch <= 128) ---------------------------------------
 enum GemvOut { GV_PARTIAL = 0, GV_RELU, GV_ARGMAX };
 
-// Tile/split choice for one decode projection: fr 16-row MFMA fragments per wave
-// (64 * fr rows per WG) and `splits` ways over K (partials; 1 when the epilogue
-// needs the full sum).
+// Work split of one decode projection.
+//   bf16: X fragment-tiled with mt row tiles, W in the inference layout; each wave
+//   owns fr 16-row fragments and a K range of kr (a multiple of 128); nwk waves per
+//   WG take consecutive K ranges and are reduced in the WG; `splits` = K / (kr nwk)
+//   partial groups remain.  fp32: `splits` ways over K.
 struct GemvPlan {
-  int fr = 2;
+  int mt = 0, fr = 0, nwk = 0, kr = 0;
   int splits = 1;
 };
-GemvPlan gemv_plan(int M, int N, int K, bool allow_split);
+// Row tiles of 16 the decode activations use for batch M (a power of two).
+int decode_mt(int M);
+GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole = false);
 
 struct GemvArgs {
   int out_mode = GV_PARTIAL;
-  int fr = 2;                     // from gemv_plan (GV_ARGMAX always uses 2)
-  int splits = 1;                 // split-K count (GV_PARTIAL only)
   float* parts = nullptr;         // GV_PARTIAL: [splits][M][N] fp32 (no bias)
   const void* bias = nullptr;     // GV_RELU
-  void* out = nullptr;            // GV_RELU: [M, N] storage type
+  void* out = nullptr;            // GV_RELU: bf16 fragment-tiled (plan mt); fp32 [M, N]
   float* logits = nullptr;        // GV_ARGMAX: optional [M, N] fp32
   float* best_val = nullptr;      // GV_ARGMAX: [M][n_blocks] per-block maxima
   int32_t* best_idx = nullptr;    // GV_ARGMAX: [M][n_blocks]
-  int n_blocks = 0;               // GV_ARGMAX: gemv_argmax_blocks(dt, N)
+  int n_blocks = 0;               // GV_ARGMAX: gemv_argmax_blocks(dt, plan, N)
   int32_t* bump = nullptr;        // GV_ARGMAX: if set, *bump += 1 once (the decode
                                   // position; this kernel never reads it)
 };
 
-// Number of column blocks the argmax epilogue produces for N columns.
-int gemv_argmax_blocks(int dt, int N);
-void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, const GemvArgs& g,
-                 hipStream_t st);
+// Y = X W^T with the chosen output (GV_RELU and GV_ARGMAX need plan.splits == 1 for bf16).
+void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, const GemvPlan& p,
+                 const GemvArgs& g, hipStream_t st);
+// Column blocks of the argmax output for N columns under plan p (also the blocking
+// of launch_reduce_argmax when p.splits > 1).
+int gemv_argmax_blocks(int dt, const GemvPlan& p, int N);
+
+// out[m][n] = round(relu(sum_s parts[s][m][n] + bias[n])) (bf16; N % 4 == 0),
+// fragment-tiled with mt row tiles (mt > 0) or row-major.
+void launch_reduce_relu(const float* parts, int S, const void* bias, void* out, int M, int N,
+                        int mt, hipStream_t st);
+// Sum S partial logits, optionally store them, and reduce each row's 128-column
+// blocks to (max, lowest index) pairs for launch_argmax_finalize; *bump += 1 once.
+void launch_reduce_argmax(const float* parts, int S, int M, int N, float* logits, float* best_val,
+                          int32_t* best_idx, int nb, int32_t* bump, hipStream_t st);
 
 // Reduce per-block argmax partials: pick[m] = lowest index among the maxima.
 // Writes pick to ids_cur[m], tokens[m * tok_stride + *pos_dev] (if tokens; the
@@ -112,10 +139,11 @@ void launch_attn_prefill(int dt, const void* q, const void* k_cache, const void*
 
 // One decode step.  qkv = sum of `splits` partials [splits][B][3d] + b_qkv: q is
 // scaled and rounded, k and v are rounded and appended at position *pos_dev;
-// attends over positions 0..*pos_dev; o [B, d] storage type.
+// attends over positions 0..*pos_dev; o [B, d] storage type, fragment-tiled with
+// x_mt row tiles when x_mt > 0.
 void launch_attn_decode(int dt, const float* qkv_parts, int splits, const void* b_qkv,
                         void* k_cache, void* v_cache, const int32_t* pos_dev, void* o,
-                        int B, int H, int D, int S_max, float q_scale, hipStream_t st);
+                        int B, int H, int D, int S_max, float q_scale, int x_mt, hipStream_t st);
 
 // *p = v (a one-thread kernel; safe next to captured work, unlike a memset node)
 void launch_set_i32(int32_t* p, int32_t v, hipStream_t st);
