@@ -113,9 +113,7 @@ def test_state_machine_generation_cycle():
     he.he_generate(ctx, P, 2, 16, 17, P)                               # 16 + 17 - 1 = 32 fits
     assert _status(he.he_generate, ctx, P, 2, 16, 18, P) == he.HE_E_RANGE
     he.he_unfuse_lora(ctx, lt)
-    # generation runs in inference mode only (adapters folded, inference layout)
-    assert _status(he.he_prefill, ctx, P, 2, 16, P) == he.HE_E_STATE
-    assert _status(he.he_generate, ctx, P, 2, 16, 16, P) == he.HE_E_STATE
+    he.he_generate(ctx, P, 2, 16, 16, P)                               # base weights, unfused
     he.he_release_cache(ctx)
     he.he_release_cache(ctx)                                           # no-op
     assert _status(he.he_decode_step, ctx, P, P) == he.HE_E_NOCACHE

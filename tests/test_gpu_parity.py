@@ -212,3 +212,29 @@ def test_opt125m_generate_greedy(c2_inputs):
     n = greedy_prefix_agrees(got[ROWS_C2, :G], picks, lg)
     log(f"opt125m greedy: {n} picks compared")
     assert n >= 8
+
+
+def test_opt125m_unfused_base_weights(c2_inputs):
+    """Generation with the adapters not folded runs the base weights (row-major):
+    first a folded run captures the decode graph in the inference layout, then after
+    the unfold the same context must re-capture and match the adapter-free oracle."""
+    params, lora, prompts, forced = c2_inputs
+    log("opt125m unfused: GPU")
+    run = GpuRun(C2, params)
+    lt = run.lora(lora)
+    with torch.cuda.stream(run.stream):
+        he.he_retake_cache(run.ctx, C2.batch, C2.max_seq)
+        he.he_fuse_lora(run.ctx, lt)
+    run.generate(prompts, 8)
+    with torch.cuda.stream(run.stream):
+        he.he_unfuse_lora(run.ctx, lt)
+    steps = [0, 1, 100, 255]
+    got = run.teacher_forced(prompts, forced, C2.gen_len, want_rows=ROWS_C2, want_steps=set(steps))
+    run.close()
+    log("opt125m unfused: oracle without adapters")
+    om = _oracle(C2, params, None)
+    seq = np.concatenate([prompts.numpy()[ROWS_C2], forced.numpy()[ROWS_C2, :C2.gen_len - 1]], axis=1)
+    full = om.forward_full(seq)
+    S = C2.prompt_len
+    for j in steps:
+        check_logits(got[j], full[:, S - 1 + j], C2.actor, f"unfused step {j}")

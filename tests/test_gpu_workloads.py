@@ -11,7 +11,7 @@ import synth
 from oracle import opt_he as O
 from transformer_decode_amd import he
 
-from gpu_util import GpuRun, check_logits, greedy_prefix_agrees, log, precision, to_dev
+from gpu_util import GpuRun, check_logits, greedy_prefix_agrees, log, oracle_floor, precision, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,8 @@ def _sampled_teacher_forced(wl, rows, steps):
     S = wl.prompt_len
     worst = 0.0
     for j in steps:
-        worst = max(worst, check_logits(got[j], full[:, S - 1 + j], wl.actor, f"{wl.name} step {j}"))
+        floors = [oracle_floor(wl.name, r, j) for r in rows]
+        worst = max(worst, check_logits(got[j], full[:, S - 1 + j], wl.actor, f"{wl.name} step {j}", floors))
     log(f"{wl.name}: max |dlogit| {worst:.3e}")
 
 

@@ -87,9 +87,11 @@ __device__ __forceinline__ size_t il_off(int n, int k, int K, int il) {
   return (size_t)((n & ~15) + (p >> lgu)) * K + (k - kb) + ((p & ((1 << lgu) - 1)) << 3) + (k & 7);
 }
 
-// Offset of lane l's 8 elements of MFMA fragment (row block rb, k-step s) in the
-// inference layout: rows 16 rb + l % 16, k = 32 s + 8 (l / 16) .. + 8.
+// Offset of lane l's 8 elements of MFMA fragment (row block rb, k-step s): rows
+// 16 rb + l % 16, k = 32 s + 8 (l / 16) .. + 8, in the inference layout or, for
+// il == 0, row-major (then a fragment is 16 row pieces of 64 bytes).
 __device__ __forceinline__ size_t il_frag(int rb, int s, int lane, int K, int il) {
+  if (il == 0) return (size_t)(rb * 16 + (lane & 15)) * K + s * 32 + ((lane >> 4) << 3);
   const int lgu = il - 3, fpb = 1 << (il - 5);         // units per block row, fragments per block
   const int q = s & (fpb - 1), p = (q << 6) | lane;
   return (size_t)(rb * 16 + (p >> lgu)) * K + ((s >> (il - 5)) << il) + ((p & ((1 << lgu) - 1)) << 3);

@@ -5,9 +5,10 @@
 // Architecture and Mode Switching": the engine keeps a single copy of the actor and
 // reconfigures it at the eval()/train() boundary).  Inference mode here means: the
 // LoRA adapters folded into the weights in place, bf16 weights switched in the same
-// pass to the inference layout the decode kernels stream (common.h, il_off), and a
-// KV workspace allocated (page 2, section 3: fuse before generate, unfuse after;
-// release the workspace after generation, re-take it before the next).  The decode step can be replayed
+// pass to the inference layout the decode kernels stream fastest (common.h, il_off),
+// and a KV workspace allocated (page 2, section 3: fuse before generate, unfuse
+// after; release the workspace after generation, re-take it before the next).
+// Generation without a fold runs the base weights in their row-major layout.  The decode step can be replayed
 // from a captured hipGraph (page 2, section 4: enable_cuda_graph), with the step's
 // position kept in device memory so that one graph serves every step.
 #include <hip/hip_runtime.h>
@@ -57,8 +58,7 @@ struct he_ctx {
   float q_scale = 1.f;
   bool validate_only = false, use_graph = true;
   bool fused = false, failed = false;
-  // weight layout while fused: inference layout of K = d and K = F weights (bf16)
-  int il_d = 0, il_f = 0;
+  int il_d = 0;                   // inference layout of the K = d weights (bf16)
   std::string err;
 
   // workspace (library-owned)
@@ -90,9 +90,11 @@ struct he_ctx {
   bool prefilled = false;
   int cur_B = 0, cur_pos = 0;
 
-  // decode graphs: [0] without logits, [1] with logits, for batch graph_B
+  // decode graphs: [0] without logits, [1] with logits, for batch graph_B and the
+  // weight layout (fused or not) they were captured with
   hipGraphExec_t graph[2] = {nullptr, nullptr};
   int graph_B = -1;
+  bool graph_fused = false;
   bool capturing = false;
 
   Timer timers[HE_K_COUNT];
@@ -201,9 +203,7 @@ static size_t parts_elems(he_ctx* c, int max_batch, int* argmax_cap) {
 }
 
 // Layout of a layer weight with K columns as the kernels must read it now.
-static int w_il(const he_ctx* c, int K) {
-  return (c->fused && c->dt == DT_BF16) ? (K == c->F ? c->il_f : c->il_d) : 0;
-}
+static int w_il(const he_ctx* c, int K) { return (c->fused && c->dt == DT_BF16) ? il_of(K) : 0; }
 static int e_il(const he_ctx* c) {
   return (c->fused && c->dt == DT_BF16 && c->desc.head == HE_HEAD_LM) ? c->il_d : 0;
 }
@@ -229,9 +229,10 @@ static const void* ln_b_after(he_ctx* c, int l) {
 
 // One decode projection into split-K partials (plan p).
 static void decode_partials(he_ctx* c, const void* X, const void* W, int B, int N, int K,
-                            const GemvPlan& p, hipStream_t st) {
+                            const GemvPlan& p, int il, hipStream_t st) {
   GemvArgs g;
   g.out_mode = GV_PARTIAL;
+  g.w_il = il;
   g.parts = c->parts;
   launch_gemv(c->dt, X, W, B, N, K, p, g, st);
 }
@@ -243,13 +244,14 @@ static void enqueue_lm_head(he_ctx* c, int B, bool want_logits) {
   hipStream_t st = c->stream;
   if (dt == DT_BF16 && c->p_lm.splits > 1) {
     run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d, [&] {
-      decode_partials(c, c->x, c->wt.tok_emb, B, c->V, d, c->p_lm, st);
+      decode_partials(c, c->x, c->wt.tok_emb, B, c->V, d, c->p_lm, e_il(c), st);
       launch_reduce_argmax(c->parts, c->p_lm.splits, B, c->V, want_logits ? c->logits : nullptr,
                            c->best_val, c->best_idx, c->n_argmax_blocks, c->pos_dev, st);
     });
   } else {
     GemvArgs g;
     g.out_mode = GV_ARGMAX;
+    g.w_il = e_il(c);
     g.logits = want_logits ? c->logits : nullptr;
     g.best_val = c->best_val;
     g.best_idx = c->best_idx;
@@ -334,30 +336,30 @@ static void enqueue_step(he_ctx* c, int B, bool want_logits, int pos) {
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
     run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * es, 2.0 * B * 3 * d * d,
-          [&] { decode_partials(c, c->x, w.w_qkv, B, 3 * d, d, c->p_qkv, st); });
+          [&] { decode_partials(c, c->x, w.w_qkv, B, 3 * d, d, c->p_qkv, w_il(c, d), st); });
     run_k(c, HE_K_ATTN_DECODE, 2.0 * B * d * es * (double)(pos + 1), 4.0 * B * d * (double)(pos + 1), [&] {
       launch_attn_decode(dt, c->parts, c->p_qkv.splits, w.b_qkv, kcache(c, l), vcache(c, l), c->pos_dev,
                          c->o, B, c->H, c->D, c->max_seq, c->q_scale, xmt, st);
     });
     run_k(c, HE_K_GEMV_DECODE, (double)d * d * es, 2.0 * B * d * d,
-          [&] { decode_partials(c, c->o, w.w_out, B, d, d, c->p_out, st); });
+          [&] { decode_partials(c, c->o, w.w_out, B, d, d, c->p_out, w_il(c, d), st); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
       launch_norm(dt, c->h, c->parts, c->p_out.splits, w.b_out, w.ln2_g, w.ln2_b, eps, c->x, B, d, 1, 0, 0,
                   xmt, st);
     });
     if (dt == DT_BF16 && c->p_fc1.splits > 1) {
       run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
-            [&] { decode_partials(c, c->x, w.w_fc1, B, F, d, c->p_fc1, st); });
+            [&] { decode_partials(c, c->x, w.w_fc1, B, F, d, c->p_fc1, w_il(c, d), st); });
       run_k(c, HE_K_EMBED_NORM, (double)B * F * 4 * c->p_fc1.splits, 0,
             [&] { launch_reduce_relu(c->parts, c->p_fc1.splits, w.b_fc1, c->a, B, F, xmt, st); });
     } else {
       GemvArgs g1;
-      g1.out_mode = GV_RELU; g1.bias = w.b_fc1; g1.out = c->a;
+      g1.out_mode = GV_RELU; g1.w_il = w_il(c, d); g1.bias = w.b_fc1; g1.out = c->a;
       run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
             [&] { launch_gemv(dt, c->x, w.w_fc1, B, F, d, c->p_fc1, g1, st); });
     }
     run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
-          [&] { decode_partials(c, c->a, w.w_fc2, B, d, F, c->p_fc2, st); });
+          [&] { decode_partials(c, c->a, w.w_fc2, B, d, F, c->p_fc2, w_il(c, F), st); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
       launch_norm(dt, c->h, c->parts, c->p_fc2.splits, w.b_fc2, ln_g_after(c, l), ln_b_after(c, l), eps,
                   c->x, B, d, 1, 0, 0, xmt, st);
@@ -502,7 +504,6 @@ he_status he_create(const he_model_desc* desc, const he_weight_table* w, void* h
   c->de = de;
   c->q_scale = (float)(1.0 / std::sqrt((double)hd));
   c->il_d = il_of(c->d);
-  c->il_f = il_of(c->F);
   c->validate_only = (D.flags & HE_FLAG_VALIDATE_ONLY) != 0;
   const char* ng = std::getenv("HE_NO_GRAPH");
   c->use_graph = D.use_graph && !(ng && ng[0] == '1');
@@ -717,14 +718,6 @@ static he_status prefill_checks(he_ctx* c, const int32_t* ids, int B, int S, con
   return HE_OK;
 }
 
-// Generation runs in inference mode only (adapters folded, bf16 weights in the
-// inference layout); checked after the arguments.
-static he_status need_inference_mode(he_ctx* c) {
-  if (!c->fused)
-    return set_err(c, HE_E_STATE, "generation runs in inference mode: call he_fuse_lora first");
-  return HE_OK;
-}
-
 static he_status do_prefill(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
   set_plans(c, B);
   launch_set_i32(c->pos_dev, S - 1, c->stream);
@@ -741,7 +734,6 @@ static he_status do_prefill(he_ctx* c, const int32_t* ids, int B, int S, bool wa
 he_status he_prefill(he_ctx* c, const int32_t* ids, int32_t B, int32_t S, int32_t* d_next, float* d_logits) {
   if (!c) return HE_E_ARG;
   he_status s = prefill_checks(c, ids, B, S, d_next);
-  if (s == HE_OK) s = need_inference_mode(c);
   if (s != HE_OK) return s;
   if (c->validate_only) {
     c->prefilled = true; c->cur_B = B; c->cur_pos = S;
@@ -766,7 +758,7 @@ static he_status run_step(he_ctx* c, bool want_logits) {
   const bool graph = c->use_graph && !any_timer_armed(c);
   if (graph) {
     hipGraphExec_t& ge = c->graph[want_logits ? 1 : 0];
-    if (c->graph_B != B) drop_graphs(c);
+    if (c->graph_B != B || c->graph_fused != c->fused) drop_graphs(c);
     if (!ge) {
       hipGraph_t g = nullptr;
       HIP_TRY(c, hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal));
@@ -779,6 +771,7 @@ static he_status run_step(he_ctx* c, bool want_logits) {
       hipGraphDestroy(g);
       if (e != hipSuccess) { ge = nullptr; return hip_fail(c, e, "hipGraphInstantiate"); }
       c->graph_B = B;
+      c->graph_fused = c->fused;
     }
     HIP_TRY(c, hipGraphLaunch(ge, c->stream));
   } else {
@@ -825,8 +818,6 @@ he_status he_generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, 
   if (S_g < 1) return set_err(c, HE_E_ARG, "S_g %d < 1", S_g);
   if (S + S_g - 1 > c->max_seq)
     return set_err(c, HE_E_RANGE, "S_p + S_g - 1 = %d exceeds max_seq %d", S + S_g - 1, c->max_seq);
-  s = need_inference_mode(c);
-  if (s != HE_OK) return s;
   if (c->validate_only) {
     c->prefilled = true; c->cur_B = B; c->cur_pos = S;
     for (int j = 1; j < S_g; ++j) {

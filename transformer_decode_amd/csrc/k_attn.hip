@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256, (D >= 64 && sizeof(T) == 2 ? 8 : 4)) void attn
   // Keys 0..pos-1 in blocks of U keys per group, double buffered: block b+1 is in
   // flight while block b is consumed.  Loads are unconditional (keys past pos-1 are
   // clamped to pos-1 and not consumed) so every path keeps the same loads in flight.
-  constexpr int U = sizeof(T) == 2 ? 1 : 1;
+  constexpr int U = 1;
   const int nblk = (pos + U * NG - 1) / (U * NG);
   Raw8<T> kr[2][U], vr[2][U];
   auto load_blk = [&](int blk, Raw8<T> (&kk)[U], Raw8<T> (&vv)[U]) {

@@ -210,17 +210,25 @@ __device__ __forceinline__ T* x_at(T* x, int row, int k, int d, int x_mt) {
   return x + (x_mt ? xt_off(row, k, x_mt) : (size_t)row * d + k);
 }
 
+// LayerNorm of one row held by the block (up to kLnChunks chunks of 4 per thread),
+// written rounded to x (and to the stream for post-LN).  Mean, then the biased
+// variance around it, as two fixed-order block reductions; gamma and beta are
+// fetched before the reductions so their latency overlaps them.
 template <typename T>
 __device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, float eps,
                                          const T* g, const T* b, T* x, int row, int x_mt,
                                          float* hrow_post, float* red) {
   const int tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
+  float gv[kLnChunks][4], bv[kLnChunks][4];
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < kLnChunks; ++c)
-    if (tid + c * nt < nch)
+    if (tid + c * nt < nch) {
+      ld4(g + (tid + c * nt) * 4, gv[c]);
+      ld4(b + (tid + c * nt) * 4, bv[c]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) s += v[c][q];
+    }
   const float mean = block_sum(s, red) / (float)d;
   float s2 = 0.f;
 #pragma unroll
@@ -234,19 +242,18 @@ __device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, 
   for (int c = 0; c < kLnChunks; ++c) {
     const int ch = tid + c * nt;
     if (ch < nch) {
-      float gv[4], bv[4], y[4];
-      ld4(g + ch * 4, gv);
-      ld4(b + ch * 4, bv);
+      float y[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) y[q] = (v[c][q] - mean) * rstd * gv[q] + bv[q];
+      for (int q = 0; q < 4; ++q) y[q] = (v[c][q] - mean) * rstd * gv[c][q] + bv[c][q];
       if (hrow_post) st4(hrow_post + ch * 4, y);   // post-LN: the stream is the norm
       st4(x_at(x, row, ch * 4, d, x_mt), y);         // GEMM input: rounded
     }
   }
 }
 
+// Threads per row: two chunks of 4 each (measured fastest at decode shapes), whole waves.
 static int ln_threads(int d) {
-  int t = (d / 4 + 63) / 64 * 64;
+  int t = (d / 8 + 63) / 64 * 64;
   return t < 64 ? 64 : (t > 1024 ? 1024 : t);
 }
 

@@ -3,9 +3,10 @@
 // Generation streams every weight once per token (paper summary, "Inference Mode:
 // Generation Phase Optimizations": generation is bound by memory bandwidth, and the
 // inference kernels lay the weights out for sequential access).  bf16 models read W
-// in the inference layout (common.h, il_off): every 16 x 32 MFMA A operand is 1 KB
-// of consecutive bytes, so one 16-byte load per lane fetches a whole fragment with
-// fully used HBM bursts.  The activations arrive fragment-tiled too (xt_off): the B
+// in the inference layout (common.h, il_off) while the adapters are folded in: every
+// 16 x 32 MFMA A operand is 1 KB of consecutive bytes, so one 16-byte load per lane
+// fetches a whole fragment with fully used HBM bursts.  Unfused base weights
+// (row-major) go through the same kernel with 64-byte pieces per row.  The activations arrive fragment-tiled too (xt_off): the B
 // operand of a k-step is 1 KB per 16 batch rows, read from L2.
 //
 //  * A wave owns FR 16-row fragments of W and a K range of kr; it keeps PD k-steps
@@ -380,7 +381,7 @@ void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, cons
                  const GemvArgs& g, hipStream_t st) {
   if (dt == DT_BF16) {
     IlArgs a;
-    a.M = M; a.N = N; a.K = K; a.il = il_of(K); a.ns = p.kr / 32;
+    a.M = M; a.N = N; a.K = K; a.il = g.w_il; a.ns = p.kr / 32;
     a.parts = g.parts; a.bias = (const bf16*)g.bias; a.out = (bf16*)g.out;
     a.logits = g.logits; a.best_val = g.best_val; a.best_idx = g.best_idx;
     a.n_blocks = g.n_blocks; a.bump = g.bump;

@@ -96,6 +96,7 @@ GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole =
 
 struct GemvArgs {
   int out_mode = GV_PARTIAL;
+  int w_il = 0;                   // bf16 W: 0 row-major, else the inference layout il_of(K)
   float* parts = nullptr;         // GV_PARTIAL: [splits][M][N] fp32 (no bias)
   const void* bias = nullptr;     // GV_RELU
   void* out = nullptr;            // GV_RELU: bf16 fragment-tiled (plan mt); fp32 [M, N]
