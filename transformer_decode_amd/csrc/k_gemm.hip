@@ -45,6 +45,61 @@ __device__ __forceinline__ void epi_store(const EpiArgs& e, int m, int n, int N,
   }
 }
 
+// Four consecutive output columns n .. n + 3 of row m (bf16 storage, n % 4 == 0),
+// the same arithmetic as epi_store element by element, with vector accesses.
+__device__ __forceinline__ void ld_bf4(const bf16* p, float* o) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
+  o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+__device__ __forceinline__ void st_bf4(bf16* p, const float* v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
+template <int MODE>
+__device__ __forceinline__ void epi_store4(const EpiArgs& e, int m, int n, int N, const float (&acc)[4]) {
+  float b[4] = {0.f, 0.f, 0.f, 0.f}, v[4];
+  if (MODE != EPI_POSADD && e.bias) ld_bf4((const bf16*)e.bias + n, b);
+  if (MODE == EPI_QKV) {
+    const int part = n / e.d, within = n - part * e.d;
+    const int head = within / e.D, dd = within - head * e.D;
+    const int bb = m / e.seq_len, t = m - bb * e.seq_len;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = acc[c] + b[c];
+    if (part == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] *= e.q_scale;
+      st_bf4((bf16*)e.q_out + (size_t)m * e.d + within, v);
+    } else {
+      bf16* cache = (bf16*)(part == 1 ? e.k_cache : e.v_cache);
+      st_bf4(cache + (((size_t)bb * e.H + head) * e.S_max + e.pos0 + t) * e.D + dd, v);
+    }
+  } else if (MODE == EPI_RESID) {
+    float4* hp = reinterpret_cast<float4*>(e.h + (size_t)m * N + n);
+    float4 h = *hp;
+    h.x += acc[0] + b[0]; h.y += acc[1] + b[1]; h.z += acc[2] + b[2]; h.w += acc[3] + b[3];
+    *hp = h;
+  } else if (MODE == EPI_RELU) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = fmaxf(acc[c] + b[c], 0.f);
+    st_bf4((bf16*)e.out + (size_t)m * N + n, v);
+  } else if (MODE == EPI_POSADD) {
+    const int t = m % e.seq_len;
+    float p[4];
+    ld_bf4((const bf16*)e.pos_emb + (size_t)(e.pos0 + t + 2) * N + n, p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = acc[c] + p[c];
+    *reinterpret_cast<float4*>(e.h + (size_t)m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+    st_bf4((bf16*)e.out + (size_t)m * N + n, v);
+  } else {
+    *reinterpret_cast<float4*>(e.out_f32 + (size_t)m * N + n) =
+        make_float4(acc[0] + b[0], acc[1] + b[1], acc[2] + b[2], acc[3] + b[3]);
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // bf16 MFMA GEMM
 // ---------------------------------------------------------------------------------
@@ -226,6 +281,178 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(const bf16* __restri
 }
 
 // ---------------------------------------------------------------------------------
+// bf16 MFMA GEMM on 32 x 32 x 16 tiles staged by LDS DMA (M, N multiples of 256,
+// K of 32).  256 x 256 macro tile, 4 waves (2 x 2), each owning 128 x 128 as 4 x 4
+// v_mfma_f32_32x32x16_bf16 tiles (accumulators in AGPRs).  With one wave per SIMD
+// this instruction sustains about 2.1 PFLOP/s where the 16 x 16 x 32 one stops
+// near 1.3 (measured).  An operand fragment is 32 rows x 16 k = 1 KB, lane l holding
+// row l % 32, k 8 (l / 32) .. + 8.  A stage is 32 k: 16 fragments of X and 16 of W.
+// Waves fill LDS with global_load_lds_dwordx4, each lane fetching its own 16 bytes
+// (8 consecutive k of one row in row-major X and in either layout of W, il_off) to
+// slot + 16 l, so operands come back with conflict-free ds_read_b128 and never pass
+// through VGPRs on the way in.  Four stages (128 KB of LDS) rotate: loads run three
+// stages ahead of the MFMAs.
+// ---------------------------------------------------------------------------------
+constexpr int FBM = 256, FBN = 256, FST = 4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void lds_dma16(const void* g, bf16* lds_slot) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_slot, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt = n (n < 64), expcnt and lgkmcnt left open (gfx9 encoding).
+#define HE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Workgroup barrier without __syncthreads' release fence (which waits for every
+// outstanding load, the prefetch DMA included).  LDS reads before it have completed
+// (each was waited for by the MFMA that used it); the asm memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int MODE, bool WIL>
+__global__ __launch_bounds__(256) void gemm_frag_kernel(const bf16* __restrict__ X,
+                                                        const bf16* __restrict__ W, int M, int N,
+                                                        int K, EpiArgs e) {
+  // [stage][operand][fragment f = ks * 8 + row tile][512 elements]
+  __shared__ __attribute__((aligned(1024))) bf16 fsm[FST * 2 * 16 * 512];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
+  const int wm = wv >> 1, wn = wv & 1;
+
+  // XCD-aware tile order (WG w runs on XCD w % 8), groups of 4 tile rows
+  const int nm = M / FBM, nn = N / FBN, T = nm * nn;
+  const int per = (T + 7) / 8;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (t >= T) return;
+  constexpr int GM = 4;
+  const int group = t / (GM * nn), first_m = group * GM;
+  const int gsz = min(nm - first_m, GM);
+  const int tm = first_m + (t % (GM * nn)) % gsz, tn = (t % (GM * nn)) / gsz;
+  const int m0 = tm * FBM, n0 = tn * FBN;
+  // Stage s (k 32 s .. + 32): this wave loads fragments f = 4 wv + q (q < 4) of each
+  // operand.  Every lane's 16 bytes are 8 consecutive k of one row, at an address
+  // that splits into a per-lane offset fixed for the kernel plus a wave-uniform
+  // offset per stage.  Row-major: row * K + 16 ks + 8 (l / 32) per lane, 32 s
+  // uniform.  Inference layout (il_off) with block width BW = 2^il: stage s sits
+  // at k-in-block kb = 32 s mod BW, which moves every unit of the fragment by
+  // (kb / 32) * 64 positions = (kb / 32) * 64 / (BW / 8) block rows, plus the
+  // block's column offset 32 s - kb.
+  const int lrow = lane & 31, lk = (lane >> 5) << 3;
+  uint32_t offa[4], offb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int f = wv * 4 + q, ks = f >> 3, tile = f & 7;
+    offa[q] = (uint32_t)((tile * 32 + lrow) * K + ks * 16 + lk);
+    if (WIL) {
+      const int il = e.w_il, lgu = il - 3;
+      const int j = lrow & 15, u = 2 * ks + (lane >> 5);            // unit within the 32-k step
+      const int pl = (u << 4) | j;                                   // position for kb = 0
+      offb[q] = (uint32_t)((tile * 32 + (lrow & 16) + (pl >> lgu)) * K + ((pl & ((1 << lgu) - 1)) << 3));
+    } else {
+      offb[q] = offa[q];
+    }
+  }
+  const long ua0 = (long)m0 * K, ub0 = (long)n0 * K;
+  auto issue = [&](int s) {
+    bf16* sa = fsm + (size_t)(s & (FST - 1)) * 2 * 16 * 512;
+    bf16* sb = sa + 16 * 512;
+    long ub = ub0 + 32L * s;
+    if (WIL) {
+      const int il = e.w_il, lgu = il - 3, kb = (32 * s) & ((1 << il) - 1);
+      ub = ub0 + (long)(((kb >> 5) << 6) >> lgu) * K + (32L * s - kb);
+    }
+    const bf16* xa = X + ua0 + 32L * s;
+    const bf16* wb = W + ub;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = wv * 4 + q;
+      lds_dma16(xa + offa[q], sa + f * 512);
+      lds_dma16(wb + offb[q], sb + f * 512);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // operands of one 16-wide k-step: b[0..3] then a[0..3] (wave tile columns, rows)
+  auto read_frags = [&](int s, int ks, bf16x8 (&r)[8]) {
+    const bf16* sa = fsm + (size_t)(s & (FST - 1)) * 2 * 16 * 512;
+    const bf16* sb = sa + 16 * 512;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const bf16x8*>(sb + (ks * 8 + wn * 4 + j) * 512 + lane * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[4 + i] = *reinterpret_cast<const bf16x8*>(sa + (ks * 8 + wm * 4 + i) * 512 + lane * 8);
+  };
+  auto mma = [&](const bf16x8 (&r)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[j], r[4 + i], acc[i][j], 0, 0, 0);
+  };
+
+  // With one wave per SIMD, instructions issue in order: the LDS reads of the next
+  // k-step are spread between the MFMAs (scheduling groups) rather than queued in
+  // front of them.  r0 holds the first 16-wide k-step of a stage, r1 the second;
+  // each is read one half-stage before its MFMAs.  The loop body is straight-line
+  // (the last stage re-reads its own first k-step instead of a next one) so the
+  // accumulators stay in place.
+  const int ns = K / 32;
+#pragma unroll
+  for (int s = 0; s < FST - 1; ++s)
+    if (s < ns) issue(s);
+  HE_WAIT_VMCNT(8 * (FST - 2));
+  barrier_keep_loads();
+  bf16x8 r0[8], r1[8];
+  read_frags(0, 0, r0);
+  for (int s = 0; s < ns; ++s) {
+    // refill the stage that s - 1 used (every wave read it before the last barrier)
+    const bool refill = s + FST - 1 < ns;
+    if (refill) issue(s + FST - 1);
+    read_frags(s, 1, r1);
+    mma(r0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+    }
+    // stage s + 1 must have landed here and in every wave before it is read
+    if (refill) HE_WAIT_VMCNT(8 * (FST - 2));
+    else HE_WAIT_VMCNT(0);
+    barrier_keep_loads();
+    read_frags(s + 1 < ns ? s + 1 : s, 0, r0);
+    mma(r1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    }
+  }
+
+  // Epilogue straight from the accumulators.  The MFMAs compute W X^T per tile (W
+  // fragment as the first operand), so lane l holds output row m = l % 32 of the
+  // tile and register 4 q + c holds column n = 8 q + 4 (l / 32) + c: four
+  // consecutive columns per register quad, stored with one vector access.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * 128 + i * 32 + lrow;
+        const int n = n0 + wn * 128 + j * 32 + q * 8 + ((lane >> 5) << 2);
+        const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        epi_store4<MODE>(e, m, n, N, v);
+      }
+}
+
+// ---------------------------------------------------------------------------------
 // fp32 tiled FMA GEMM (16 x 16 threads, 64 x 64 tile, 4 x 4 outputs per thread)
 // ---------------------------------------------------------------------------------
 template <int MODE>
@@ -268,6 +495,14 @@ template <int MODE>
 static void gemm_dispatch(int dt, const void* X, const void* W, int M, int N, int K,
                           const EpiArgs& e, hipStream_t st) {
   if (dt == DT_BF16) {
+    if (M % FBM == 0 && N % FBN == 0 && K % 32 == 0) {
+      const int blocks = ((M / FBM) * (N / FBN) + 7) / 8 * 8;
+      if (e.w_il)
+        gemm_frag_kernel<MODE, true><<<blocks, 256, 0, st>>>((const bf16*)X, (const bf16*)W, M, N, K, e);
+      else
+        gemm_frag_kernel<MODE, false><<<blocks, 256, 0, st>>>((const bf16*)X, (const bf16*)W, M, N, K, e);
+      return;
+    }
     const long big_tiles = (long)((M + LBM - 1) / LBM) * ((N + LBN - 1) / LBN);
     if (big_tiles >= 256) {       // enough 256 x 256 tiles to cover the CUs
       const int blocks = (int)((big_tiles + 7) / 8 * 8);
