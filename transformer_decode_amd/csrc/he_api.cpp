@@ -174,7 +174,7 @@ static bool any_timer_armed(const he_ctx* c) {
 }
 
 static void set_plans(he_ctx* c, int B) {
-  c->p_qkv = decode_plan(c->dt, B, 3 * c->d, c->d, true);
+  c->p_qkv = decode_plan(c->dt, B, 3 * c->d, c->d, true, c->dt == DT_BF16);   // bf16: fused QKV epilogue
   c->p_out = decode_plan(c->dt, B, c->d, c->d, true);
   c->p_fc1 = decode_plan(c->dt, B, c->F, c->d, true);
   c->p_fc2 = decode_plan(c->dt, B, c->d, c->F, true);
@@ -190,7 +190,7 @@ static size_t parts_elems(he_ctx* c, int max_batch, int* argmax_cap) {
   int nb = 0;
   auto room = [&](const GemvPlan& p, int B, int N) { return (size_t)p.splits * (size_t)B * (size_t)N; };
   for (int B = 1; B <= max_batch; ++B) {
-    need = std::max(need, room(decode_plan(c->dt, B, 3 * c->d, c->d, true), B, 3 * c->d));
+    need = std::max(need, room(decode_plan(c->dt, B, 3 * c->d, c->d, true, c->dt == DT_BF16), B, 3 * c->d));
     need = std::max(need, room(decode_plan(c->dt, B, c->d, c->d, true), B, c->d));
     need = std::max(need, room(decode_plan(c->dt, B, c->F, c->d, true), B, c->F));
     need = std::max(need, room(decode_plan(c->dt, B, c->d, c->F, true), B, c->d));
@@ -335,12 +335,25 @@ static void enqueue_step(he_ctx* c, int B, bool want_logits, int pos) {
   });
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
-    run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * es, 2.0 * B * 3 * d * d,
-          [&] { decode_partials(c, c->x, w.w_qkv, B, 3 * d, d, c->p_qkv, w_il(c, d), st); });
-    run_k(c, HE_K_ATTN_DECODE, 2.0 * B * d * es * (double)(pos + 1), 4.0 * B * d * (double)(pos + 1), [&] {
-      launch_attn_decode(dt, c->parts, c->p_qkv.splits, w.b_qkv, kcache(c, l), vcache(c, l), c->pos_dev,
-                         c->o, B, c->H, c->D, c->max_seq, c->q_scale, xmt, st);
-    });
+    if (dt == DT_BF16) {   // q, k, v finished in the projection's epilogue
+      GemvArgs g;
+      g.out_mode = GV_QKV; g.w_il = w_il(c, d); g.bias = w.b_qkv;
+      g.q_out = c->q; g.k_cache = kcache(c, l); g.v_cache = vcache(c, l); g.pos_dev = c->pos_dev;
+      g.d = d; g.H = c->H; g.D = c->D; g.S_max = c->max_seq; g.q_scale = c->q_scale;
+      run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * es, 2.0 * B * 3 * d * d,
+            [&] { launch_gemv(dt, c->x, w.w_qkv, B, 3 * d, d, c->p_qkv, g, st); });
+      run_k(c, HE_K_ATTN_DECODE, 2.0 * B * d * es * (double)(pos + 1), 4.0 * B * d * (double)(pos + 1), [&] {
+        launch_attn_decode_q(dt, c->q, kcache(c, l), vcache(c, l), c->pos_dev, c->o, B, c->H, c->D,
+                             c->max_seq, xmt, st);
+      });
+    } else {
+      run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * es, 2.0 * B * 3 * d * d,
+            [&] { decode_partials(c, c->x, w.w_qkv, B, 3 * d, d, c->p_qkv, w_il(c, d), st); });
+      run_k(c, HE_K_ATTN_DECODE, 2.0 * B * d * es * (double)(pos + 1), 4.0 * B * d * (double)(pos + 1), [&] {
+        launch_attn_decode(dt, c->parts, c->p_qkv.splits, w.b_qkv, kcache(c, l), vcache(c, l), c->pos_dev,
+                           c->o, B, c->H, c->D, c->max_seq, c->q_scale, xmt, st);
+      });
+    }
     run_k(c, HE_K_GEMV_DECODE, (double)d * d * es, 2.0 * B * d * d,
           [&] { decode_partials(c, c->o, w.w_out, B, d, d, c->p_out, w_il(c, d), st); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {

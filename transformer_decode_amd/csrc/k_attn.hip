@@ -67,9 +67,14 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <typename T, int D>
+// QIN: q arrives finished ([B, d], scaled, rounded) and the step's k and v are
+// already in the cache at `pos` (the QKV projection's epilogue put them there), so
+// keys 0..pos all stream from the cache; otherwise q, k and v are finished here from
+// the projection's split-K partials and k, v appended.
+template <typename T, int D, bool QIN>
 __global__ __launch_bounds__(256, (D >= 64 && sizeof(T) == 2 ? 8 : 4)) void attn_decode_kernel(const float* __restrict__ parts,
                                                           int nsplit, const T* __restrict__ bqkv,
+                                                          const T* __restrict__ qin,
                                                           T* __restrict__ kc, T* __restrict__ vc,
                                                           const int32_t* __restrict__ pos_dev,
                                                           T* __restrict__ o, int B, int H,
@@ -85,9 +90,32 @@ __global__ __launch_bounds__(256, (D >= 64 && sizeof(T) == 2 ? 8 : 4)) void attn
   const int d = H * D;
   const int pos = *pos_dev;
   const size_t head_base = ((size_t)b * H + h) * S_max * D;
+  const int grp = tid / LPK, j = tid - grp * LPK;
+  const T* kb = kc + head_base + j * 8;
+  const T* vb = vc + head_base + j * 8;
+  const int nkeys = QIN ? pos + 1 : pos;   // keys streamed from the cache
+
+  // Keys in blocks of U keys per group, double buffered: block b+1 is in flight
+  // while block b is consumed.  Loads are unconditional (keys past the last are
+  // clamped to it and not consumed) so every path keeps the same loads in flight.
+  constexpr int U = 1;
+  const int nblk = (nkeys + U * NG - 1) / (U * NG);
+  Raw8<T> kr[2][U], vr[2][U];
+  auto load_blk = [&](int blk, Raw8<T> (&kk)[U], Raw8<T> (&vv)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = min(grp + NG * (blk * U + u), nkeys - 1);
+      kk[u].load(kb + (size_t)key * D);
+      vv[u].load(vb + (size_t)key * D);
+    }
+  };
+  if (QIN) {     // the cache stream starts before q is fetched
+    load_blk(0, kr[0], vr[0]);
+    for (int i = tid; i < D; i += 256) qs[i] = ld(qin + (size_t)b * d + h * D + i);
+  }
 
   // 1. finish q, k, v of this step and append k, v at `pos`
-  for (int i = tid; i < D; i += 256) {
+  for (int i = tid; i < D && !QIN; i += 256) {
     const int c = h * D + i;
     float q = 0.f, k = 0.f, v = 0.f;
     for (int s0 = 0; s0 < nsplit; s0 += 8) {     // 8 splits' loads in flight, summed in order
@@ -115,8 +143,7 @@ __global__ __launch_bounds__(256, (D >= 64 && sizeof(T) == 2 ? 8 : 4)) void attn
   }
   __syncthreads();
 
-  // 2. stream keys 0..pos-1 from the cache; the new key (pos) comes from LDS
-  const int grp = tid / LPK, j = tid - grp * LPK;
+  // 2. stream keys from the cache (without QIN the new key, pos, comes from LDS)
   float qv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qv[e] = qs[j * 8 + e];
@@ -137,22 +164,6 @@ __global__ __launch_bounds__(256, (D >= 64 && sizeof(T) == 2 ? 8 : 4)) void attn
     return group_sum<LPK>(s);
   };
 
-  const T* kb = kc + head_base + j * 8;
-  const T* vb = vc + head_base + j * 8;
-  // Keys 0..pos-1 in blocks of U keys per group, double buffered: block b+1 is in
-  // flight while block b is consumed.  Loads are unconditional (keys past pos-1 are
-  // clamped to pos-1 and not consumed) so every path keeps the same loads in flight.
-  constexpr int U = 1;
-  const int nblk = (pos + U * NG - 1) / (U * NG);
-  Raw8<T> kr[2][U], vr[2][U];
-  auto load_blk = [&](int blk, Raw8<T> (&kk)[U], Raw8<T> (&vv)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int key = min(grp + NG * (blk * U + u), pos - 1);
-      kk[u].load(kb + (size_t)key * D);
-      vv[u].load(vb + (size_t)key * D);
-    }
-  };
   auto use_blk = [&](int blk, const Raw8<T> (&kk)[U], const Raw8<T> (&vv)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -161,11 +172,11 @@ __global__ __launch_bounds__(256, (D >= 64 && sizeof(T) == 2 ? 8 : 4)) void attn
       kk[u].unpack(kv);
       vv[u].unpack(vx);
       const float sc = dot(kv);           // all lanes of the group take part
-      if (key < pos) consume(sc, vx);
+      if (key < nkeys) consume(sc, vx);
     }
   };
-  if (pos > 0) {
-    load_blk(0, kr[0], vr[0]);
+  if (nkeys > 0) {
+    if (!QIN) load_blk(0, kr[0], vr[0]);
     for (int b = 0; b < nblk; b += 2) {
       load_blk(b + 1, kr[1], vr[1]);
       __builtin_amdgcn_sched_barrier(0);   // issue the next block before using this one
@@ -175,7 +186,7 @@ __global__ __launch_bounds__(256, (D >= 64 && sizeof(T) == 2 ? 8 : 4)) void attn
       if (b + 1 < nblk) use_blk(b + 1, kr[1], vr[1]);
     }
   }
-  if (grp == pos % NG) {
+  if (!QIN && grp == pos % NG) {
     float kv[8], vv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { kv[e] = kn[j * 8 + e]; vv[e] = vn[j * 8 + e]; }
@@ -204,9 +215,10 @@ void launch_attn_decode(int dt, const float* qkv_parts, int splits, const void* 
                         void* k_cache, void* v_cache, const int32_t* pos_dev, void* o, int B,
                         int H, int D, int S_max, float q_scale, int x_mt, hipStream_t st) {
 #define HE_DEC(T, DD)                                                                         \
-  attn_decode_kernel<T, DD><<<B * H, 256, 0, st>>>(qkv_parts, splits, (const T*)b_qkv,        \
-                                                   (T*)k_cache, (T*)v_cache, pos_dev, (T*)o, B, \
-                                                   H, S_max, q_scale, XMT)
+  attn_decode_kernel<T, DD, false><<<B * H, 256, 0, st>>>(qkv_parts, splits, (const T*)b_qkv,  \
+                                                          nullptr, (T*)k_cache, (T*)v_cache,    \
+                                                          pos_dev, (T*)o, B, H, S_max, q_scale, \
+                                                          XMT)
   if (dt == DT_BF16) {
     const int XMT = x_mt;
     switch (D) {
@@ -225,6 +237,31 @@ void launch_attn_decode(int dt, const float* qkv_parts, int splits, const void* 
     }
   }
 #undef HE_DEC
+}
+
+void launch_attn_decode_q(int dt, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* pos_dev, void* o, int B, int H, int D, int S_max,
+                          int x_mt, hipStream_t st) {
+#define HE_DECQ(T, DD)                                                                              \
+  attn_decode_kernel<T, DD, true><<<B * H, 256, 0, st>>>(nullptr, 0, nullptr, (const T*)q,          \
+                                                         (T*)k_cache, (T*)v_cache, pos_dev, (T*)o, \
+                                                         B, H, S_max, 1.f, x_mt)
+  if (dt == DT_BF16) {
+    switch (D) {
+      case 16: HE_DECQ(bf16, 16); break;
+      case 32: HE_DECQ(bf16, 32); break;
+      case 64: HE_DECQ(bf16, 64); break;
+      default: HE_DECQ(bf16, 128); break;
+    }
+  } else {
+    switch (D) {
+      case 16: HE_DECQ(float, 16); break;
+      case 32: HE_DECQ(float, 32); break;
+      case 64: HE_DECQ(float, 64); break;
+      default: HE_DECQ(float, 128); break;
+    }
+  }
+#undef HE_DECQ
 }
 
 // ---------------------------------------------------------------------------------

@@ -15,7 +15,9 @@
 //    they reduce through LDS in a fixed wave order, so split-K leaves K / (kr NWK)
 //    partial groups (often one) for the consumer to sum, also in a fixed order.
 //  * Epilogues: fp32 partials; bias + ReLU rounded into the next projection's tiled
-//    activations (one group only); per-WG greedy argmax (+ optional logits).
+//    activations (one group only); bias, q scaling and rounding with the k and v of
+//    the step appended to the KV cache (one group only); per-WG greedy argmax (+
+//    optional logits).
 // fp32 models (the tiny workload) use a plain FMA kernel on row-major weights.
 #include <utility>
 
@@ -72,9 +74,15 @@ GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole) 
     }
     return false;
   };
-  if (whole) {   // one group: a K range of K / nwk per wave
-    for (int nwk = 1; nwk <= 4; nwk *= 2)
-      if (K % (128 * nwk) == 0 && choose(K / nwk, false)) return p;
+  if (whole) {   // one group: the most rows per wave, the fewest waves per WG (1, 2, 4)
+                 // that put >= 512 waves in flight, a K range of K / nwk each
+    const long rg = (nrb + frmax - 1) / frmax;
+    int nwk = 1;
+    while (nwk < 4 && rg * nwk < 512 && K % (128 * nwk * 2) == 0) nwk *= 2;
+    if (K % (128 * nwk) == 0) {
+      p.fr = frmax; p.nwk = nwk; p.kr = K / nwk; p.splits = 1;
+      return p;
+    }
   }
   if (allow_split) {
     for (int kr = 1024; kr >= 128; kr >>= 1)
@@ -117,6 +125,12 @@ struct IlArgs {
   int32_t* best_idx;
   int n_blocks;
   int32_t* bump;
+  bf16* q_out;                    // QKV
+  bf16* k_cache;
+  bf16* v_cache;
+  const int32_t* pos_dev;
+  int d, H, D, S_max;
+  float q_scale;
 };
 
 constexpr int kPD = 3;            // k-steps of loads in flight ahead of the MFMAs
@@ -185,6 +199,25 @@ __global__ __launch_bounds__(NWK * 64) void gemv_il_kernel(const bf16* __restric
       u.x = (uint32_t)f2bf(fmaxf(v[0] + b4[0], 0.f)) | ((uint32_t)f2bf(fmaxf(v[1] + b4[1], 0.f)) << 16);
       u.y = (uint32_t)f2bf(fmaxf(v[2] + b4[2], 0.f)) | ((uint32_t)f2bf(fmaxf(v[3] + b4[3], 0.f)) << 16);
       *reinterpret_cast<uint2*>(a.out + xt_off(m, n, MT)) = u;
+    } else if (OUT == GV_QKV) {
+      // four consecutive columns of one of q, k, v (D % 4 == 0): one head, one 8-byte store
+      const uint2 bb = *reinterpret_cast<const uint2*>(a.bias + n);
+      float w[4] = {v[0] + __uint_as_float(bb.x << 16), v[1] + __uint_as_float(bb.x & 0xffff0000u),
+                    v[2] + __uint_as_float(bb.y << 16), v[3] + __uint_as_float(bb.y & 0xffff0000u)};
+      const int part = n / a.d, within = n - part * a.d;
+      bf16* dst;
+      if (part == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w[c] *= a.q_scale;
+        dst = a.q_out + (size_t)m * a.d + within;
+      } else {
+        const int head = within / a.D, dd = within - head * a.D;
+        dst = (part == 1 ? a.k_cache : a.v_cache) + (((size_t)m * a.H + head) * a.S_max + *a.pos_dev) * a.D + dd;
+      }
+      uint2 u;
+      u.x = (uint32_t)f2bf(w[0]) | ((uint32_t)f2bf(w[1]) << 16);
+      u.y = (uint32_t)f2bf(w[2]) | ((uint32_t)f2bf(w[3]) << 16);
+      *reinterpret_cast<uint2*>(dst) = u;
     } else {
       if (a.logits) *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.N + n) = v;
     }
@@ -243,6 +276,7 @@ static void il_launch(int out, const bf16* X, const bf16* W, const IlArgs& a, in
   dim3 grid((a.N / 16 + FR - 1) / FR, splits);
   if (out == GV_PARTIAL) gemv_il_kernel<MT, FR, NWK, GV_PARTIAL><<<grid, NWK * 64, 0, st>>>(X, W, a);
   else if (out == GV_RELU) gemv_il_kernel<MT, FR, NWK, GV_RELU><<<grid, NWK * 64, 0, st>>>(X, W, a);
+  else if (out == GV_QKV) gemv_il_kernel<MT, FR, NWK, GV_QKV><<<grid, NWK * 64, 0, st>>>(X, W, a);
   else gemv_il_kernel<MT, FR, NWK, GV_ARGMAX><<<grid, NWK * 64, 0, st>>>(X, W, a);
 }
 
@@ -385,6 +419,8 @@ void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, cons
     a.parts = g.parts; a.bias = (const bf16*)g.bias; a.out = (bf16*)g.out;
     a.logits = g.logits; a.best_val = g.best_val; a.best_idx = g.best_idx;
     a.n_blocks = g.n_blocks; a.bump = g.bump;
+    a.q_out = (bf16*)g.q_out; a.k_cache = (bf16*)g.k_cache; a.v_cache = (bf16*)g.v_cache;
+    a.pos_dev = g.pos_dev; a.d = g.d; a.H = g.H; a.D = g.D; a.S_max = g.S_max; a.q_scale = g.q_scale;
     const bf16* x = (const bf16*)X;
     const bf16* w = (const bf16*)W;
     switch (p.mt) {

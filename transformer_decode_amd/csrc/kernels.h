@@ -79,7 +79,7 @@ void launch_gemm(int dt, const void* X, const void* W, int M, int N, int K, cons
                  hipStream_t st);
 
 // ---- decode-shaped GEMM (M = batch <= 128) ---------------------------------------
-enum GemvOut { GV_PARTIAL = 0, GV_RELU, GV_ARGMAX };
+enum GemvOut { GV_PARTIAL = 0, GV_RELU, GV_ARGMAX, GV_QKV };
 
 // Work split of one decode projection.
 //   bf16: X fragment-tiled with mt row tiles, W in the inference layout; each wave
@@ -106,9 +106,19 @@ struct GemvArgs {
   int n_blocks = 0;               // GV_ARGMAX: gemv_argmax_blocks(dt, plan, N)
   int32_t* bump = nullptr;        // GV_ARGMAX: if set, *bump += 1 once (the decode
                                   // position; this kernel never reads it)
+  // GV_QKV (bf16, plan.splits == 1): rows n of the packed [q; k; v] projection plus
+  // bias; q scaled and rounded into q_out [M][d], k and v rounded and appended to
+  // the layer's cache [B_max][H][S_max][D] at position *pos_dev
+  void* q_out = nullptr;
+  void* k_cache = nullptr;
+  void* v_cache = nullptr;
+  const int32_t* pos_dev = nullptr;
+  int d = 0, H = 0, D = 0, S_max = 0;
+  float q_scale = 1.f;
 };
 
-// Y = X W^T with the chosen output (GV_RELU and GV_ARGMAX need plan.splits == 1 for bf16).
+// Y = X W^T with the chosen output (GV_RELU, GV_ARGMAX and GV_QKV need plan.splits == 1
+// for bf16; GV_QKV is bf16 only).
 void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, const GemvPlan& p,
                  const GemvArgs& g, hipStream_t st);
 // Column blocks of the argmax output for N columns under plan p (also the blocking
@@ -145,6 +155,11 @@ void launch_attn_prefill(int dt, const void* q, const void* k_cache, const void*
 void launch_attn_decode(int dt, const float* qkv_parts, int splits, const void* b_qkv,
                         void* k_cache, void* v_cache, const int32_t* pos_dev, void* o,
                         int B, int H, int D, int S_max, float q_scale, int x_mt, hipStream_t st);
+// The same step when q is finished ([B, d] storage type, scaled) and this step's k
+// and v are already in the cache at *pos_dev (GV_QKV): attends over 0..*pos_dev.
+void launch_attn_decode_q(int dt, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* pos_dev, void* o, int B, int H, int D, int S_max,
+                          int x_mt, hipStream_t st);
 
 // *p = v (a one-thread kernel; safe next to captured work, unlike a memset node)
 void launch_set_i32(int32_t* p, int32_t v, hipStream_t st);
