@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+CAL_BYTES = 512 << 20      # calibration copy for the byte counters: 512 MiB read, 512 MiB written
 BF16_PEAK = 2.5e15         # MI355X dense bf16 MFMA, flop/s
 METRIC = "experience-gen tokens/s + decode HBM roofline %, OPT-6.7B-shape b64 256->256"
 
@@ -123,6 +124,89 @@ def cpu_baseline(wl, seed=0, layers=2, rows=(0, 1, 32, 63), steps=4):
     }
 
 
+# ---------------------------------------------------------------------------------
+# rocprofv3 output -> committed summaries (profiles/)
+# ---------------------------------------------------------------------------------
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["transformer_decode_amd/csrc/k_gemv.hip", "transformer_decode_amd/csrc/k_attn.hip",
+                  "transformer_decode_amd/csrc/k_elem.hip", "transformer_decode_amd/csrc/common.h"]
+
+
+def kernel_class(name):
+    """The bench's kernel classes, from a kernel's demangled name."""
+    if "gemv_il_kernel" in name or "gemv_f32_kernel" in name:
+        return "lmhead" if (name.rstrip(")").split(">")[0].endswith(", 2") or "ARGMAX" in name) else "gemv_decode"
+    if "attn_decode_kernel" in name:
+        return "attn_decode"
+    if "gemm_" in name:
+        return "gemm_prefill"
+    if "attn_prefill" in name:
+        return "attn_prefill"
+    if "lora" in name:
+        return "lora"
+    if "norm_kernel" in name or "embed_" in name or "reduce_" in name:
+        return "embed_norm"
+    return "other"
+
+
+def sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counters_summary(fetch_csv, write_csv, workload, command):
+    """Per-class HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the counter reads for the calibration copy of
+    CAL_BYTES (the runtime's copy kernel, the dispatches of that size)."""
+    import csv
+    out = {"workload": workload, "command": command, "sources_sha": sources_sha(), "classes": {}}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = list(csv.DictReader(open(path)))
+        cal = [float(r["Counter_Value"]) * 1024 for r in rows if "copyBuffer" in r["Kernel_Name"]
+               and float(r["Counter_Value"]) * 1024 > CAL_BYTES / 4]
+        factor = CAL_BYTES / (sum(cal) / len(cal)) if cal else None
+        out[f"{key}_factor"] = factor
+        out[f"{key}_calibration_readings_bytes"] = cal
+        acc = {}
+        for r in rows:
+            c = kernel_class(r["Kernel_Name"])
+            acc.setdefault(c, []).append(float(r["Counter_Value"]) * 1024)
+        for c, v in acc.items():
+            e = out["classes"].setdefault(c, {})
+            e[f"{key}_raw_bytes_per_dispatch"] = sum(v) / len(v)
+            e[f"{key}_bytes_per_dispatch"] = sum(v) / len(v) * (factor or float("nan"))
+            e["dispatches"] = len(v)
+    for e in out["classes"].values():
+        e["traffic_bytes_per_dispatch"] = e.get("fetch_bytes_per_dispatch", 0.0) + e.get("write_bytes_per_dispatch", 0.0)
+    return out
+
+
+def stats_summary(stats_csv, workload, command):
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# Kernel time, {workload}", "", "Command (run from the repository root, output under gpurun_out/):", "",
+             "```", command, "```", "",
+             "| kernel | calls | avg us | total ms | share |", "|---|---|---|---|---|"]
+    cls = {}
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        n = r["Name"]
+        lines.append(f"| `{n[:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['TotalDurationNs']) / tot * 100:.1f}% |")
+        c = cls.setdefault(kernel_class(n), [0, 0.0])
+        c[0] += int(r["Calls"])
+        c[1] += float(r["TotalDurationNs"])
+    lines += ["", "Per class (the bench's kernel classes):", "", "| class | calls | avg us | total ms |", "|---|---|---|---|"]
+    for c, (n, t) in sorted(cls.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| {c} | {n} | {t / n / 1e3:.2f} | {t / 1e6:.2f} |")
+    lines.append(f"\nTotal kernel time {tot / 1e6:.1f} ms.")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,9 +218,28 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-phase / per-kernel passes")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--trace-steps", type=int, default=0,
-                    help="for counter collection: run fuse + prefill + N decode steps + unfuse once, "
-                         "print nothing and exit")
+                    help="for counter collection: a calibration copy, then fuse + prefill + N decode "
+                         "steps + unfuse once; prints nothing and exits")
+    ap.add_argument("--counters-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection.csv files into "
+                         "the per-class traffic summary (no GPU)")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
+                    help="turn a rocprofv3 --stats kernel_stats.csv into a markdown summary (no GPU)")
+    ap.add_argument("--command", default="", help="the command that produced the csv (recorded)")
     args = ap.parse_args()
+
+    if args.counters_summary:
+        f, w, o = args.counters_summary
+        summ = counters_summary(f, w, args.workload, args.command)
+        with open(o, "w") as fh:
+            json.dump(summ, fh, indent=1)
+        print(json.dumps(summ["classes"], indent=1))
+        return
+    if args.stats_summary:
+        st_csv, o = args.stats_summary
+        with open(o, "w") as fh:
+            fh.write(stats_summary(st_csv, args.workload, args.command))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -179,6 +282,14 @@ def main():
     t_retake = time.time() - t
 
     if args.trace_steps:
+        # calibration for the byte counters: a plain copy of known size (torch's own
+        # copy kernel) before the traced steps
+        src = torch.ones(CAL_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
         nxt = torch.empty(B, dtype=torch.int32, device="cuda")
         with torch.cuda.stream(st):
             he.he_fuse_lora(ctx, lt)
@@ -202,18 +313,18 @@ def main():
             step()
         he.he_sync(ctx)
         log("warmup done")
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
-        ev0.record(st)
+        evs[0].record(st)
         w0 = time.time()
-        for _ in range(args.steps):
+        for i in range(args.steps):
             step()
-        ev1.record(st)
+            evs[i + 1].record(st)
         he.he_sync(ctx)
         torch.cuda.synchronize()
         wall = time.time() - w0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
     value = B * G / (ms / 1e3)
     log(f"timed {args.steps} steps: {ms:.1f} ms/step (wall {wall / args.steps * 1e3:.1f} ms/step)")
 
@@ -222,6 +333,7 @@ def main():
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if a.dtype == "bf16" else "f32", "data": "synthetic",
+        "ms_per_step_each": per_step, "ms_per_step_median": sorted(per_step)[len(per_step) // 2],
         "config": {"workload": f"{wl.name}-shape actor, batch {B}, prompt {S}, generate {G} greedy, "
                                f"LoRA rank {wl.lora_rank} fused before / unfused after",
                    "layers": a.n_layers, "d_model": a.d_model, "heads": a.n_heads, "ffn": a.d_ffn,
@@ -287,9 +399,17 @@ def main():
         s = stats[dom]
         avg_s = s.total_ms / s.launches / 1e3
         per_launch = s.bytes / s.launches
+        traffic, traffic_src = None, None
+        cpath = os.path.join(PROFILES, f"counters_decode_{args.workload}_b{B}.json")
+        if os.path.exists(cpath):
+            summ = json.load(open(cpath))
+            if summ.get("sources_sha") == sources_sha() and dom in summ.get("classes", {}):
+                traffic = summ["classes"][dom]["traffic_bytes_per_dispatch"]
+                traffic_src = os.path.relpath(cpath, ROOT)
         res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": per_launch / avg_s / 1e9,
                            "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                           "frac": per_launch / avg_s / HBM_PEAK, "traffic": None,
+                           "frac": per_launch / avg_s / HBM_PEAK, "traffic": traffic,
+                           "traffic_source": traffic_src,
                            "bytes_per_launch": per_launch, "avg_launch_us": avg_s * 1e6,
                            "launches": s.launches}
         log(f"roofline: {json.dumps(res['roofline'])}")
@@ -298,6 +418,31 @@ def main():
         he.he_release_cache(ctx)
         he.he_sync(ctx)
     eng.close()
+
+    if not args.no_breakdown and not args.no_graph:
+        # the same decode phase launched directly (no hipGraph replay), for the graph gain
+        eng2 = he.Engine(a, dev, use_graph=False)
+        ctx2, st2 = eng2.ctx, eng2.stream
+        lt2, _keep2 = eng2.lora(ldev, wl.lora_rank, wl.lora_alpha)
+        with torch.cuda.stream(st2):
+            he.he_retake_cache(ctx2, B, wl.max_seq)
+            he.he_fuse_lora(ctx2, lt2)
+            nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+            E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            he.he_prefill(ctx2, prompts.data_ptr(), B, S, nxt.data_ptr(), 0)
+            E[0].record(st2)
+            for _ in range(G - 1):
+                he.he_decode_step(ctx2, nxt.data_ptr(), nxt.data_ptr(), 0)
+            E[1].record(st2)
+            he.he_unfuse_lora(ctx2, lt2)
+            he.he_release_cache(ctx2)
+            he.he_sync(ctx2)
+            torch.cuda.synchronize()
+        eng2.close()
+        t_dec_direct = E[0].elapsed_time(E[1]) / 1e3
+        res["phases"]["decode_ms_no_graph"] = t_dec_direct * 1e3
+        res["phases"]["graph_speedup"] = t_dec_direct / (res["phases"]["decode_ms"] / 1e3)
+        log(f"decode without graph: {t_dec_direct * 1e3:.1f} ms (graph gain x{res['phases']['graph_speedup']:.3f})")
 
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")

@@ -1,6 +1,7 @@
 // Device-side helpers shared by the HIP kernels of libhe (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -159,9 +159,21 @@ static void run_k(he_ctx* c, int kclass, double bytes, double flops, Fn&& fn) {
       return;
     }
   }
-  hipEventRecord(ev.first, c->stream);
-  fn();
-  hipEventRecord(ev.second, c->stream);
+  if (kclass == HE_K_GEMV_DECODE || kclass == HE_K_ATTN_DECODE) {
+    // a single kernel whose launch takes the timestamps itself
+    g_launch_timer = LaunchTimer{ev.first, ev.second};
+    fn();
+    const bool consumed = g_launch_timer.start == nullptr;
+    g_launch_timer = LaunchTimer{};
+    if (!consumed) {   // launched some other way: no sample
+      t.pool.push_back(ev);
+      return;
+    }
+  } else {
+    hipEventRecord(ev.first, c->stream);
+    fn();
+    hipEventRecord(ev.second, c->stream);
+  }
   t.live.push_back(ev);
   t.bytes.push_back(bytes);
   t.flops.push_back(flops);

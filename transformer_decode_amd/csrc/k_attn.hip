@@ -242,10 +242,20 @@ void launch_attn_decode(int dt, const float* qkv_parts, int splits, const void* 
 void launch_attn_decode_q(int dt, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* pos_dev, void* o, int B, int H, int D, int S_max,
                           int x_mt, hipStream_t st) {
-#define HE_DECQ(T, DD)                                                                              \
-  attn_decode_kernel<T, DD, true><<<B * H, 256, 0, st>>>(nullptr, 0, nullptr, (const T*)q,          \
-                                                         (T*)k_cache, (T*)v_cache, pos_dev, (T*)o, \
-                                                         B, H, S_max, 1.f, x_mt)
+#define HE_DECQ(T, DD)                                                                                      \
+  do {                                                                                                      \
+    if (g_launch_timer.start) {                                                                            \
+      hipExtLaunchKernelGGL(attn_decode_kernel<T, DD, true>, dim3(B * H), dim3(256), 0, st,               \
+                            g_launch_timer.start, g_launch_timer.stop, 0, (const float*)nullptr, 0,       \
+                            (const T*)nullptr, (const T*)q, (T*)k_cache, (T*)v_cache, pos_dev, (T*)o, B, \
+                            H, S_max, 1.f, x_mt);                                                         \
+      g_launch_timer = LaunchTimer{};                                                                       \
+    } else {                                                                                                \
+      attn_decode_kernel<T, DD, true><<<B * H, 256, 0, st>>>(nullptr, 0, nullptr, (const T*)q,            \
+                                                             (T*)k_cache, (T*)v_cache, pos_dev, (T*)o,   \
+                                                             B, H, S_max, 1.f, x_mt);                     \
+    }                                                                                                       \
+  } while (0)
   if (dt == DT_BF16) {
     switch (D) {
       case 16: HE_DECQ(bf16, 16); break;

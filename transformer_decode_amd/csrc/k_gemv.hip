@@ -270,14 +270,28 @@ __global__ __launch_bounds__(NWK * 64) void gemv_il_kernel(const bf16* __restric
   }
 }
 
+thread_local LaunchTimer g_launch_timer;
+
+template <class Kern>
+static void timed_launch(Kern k, dim3 grid, dim3 block, hipStream_t st, const bf16* X, const bf16* W,
+                         const IlArgs& a) {
+  if (g_launch_timer.start) {
+    hipExtLaunchKernelGGL(k, grid, block, 0, st, g_launch_timer.start, g_launch_timer.stop, 0, X, W, a);
+    g_launch_timer = LaunchTimer{};
+  } else {
+    k<<<grid, block, 0, st>>>(X, W, a);
+  }
+}
+
 template <int MT, int FR, int NWK>
 static void il_launch(int out, const bf16* X, const bf16* W, const IlArgs& a, int splits,
                       hipStream_t st) {
   dim3 grid((a.N / 16 + FR - 1) / FR, splits);
-  if (out == GV_PARTIAL) gemv_il_kernel<MT, FR, NWK, GV_PARTIAL><<<grid, NWK * 64, 0, st>>>(X, W, a);
-  else if (out == GV_RELU) gemv_il_kernel<MT, FR, NWK, GV_RELU><<<grid, NWK * 64, 0, st>>>(X, W, a);
-  else if (out == GV_QKV) gemv_il_kernel<MT, FR, NWK, GV_QKV><<<grid, NWK * 64, 0, st>>>(X, W, a);
-  else gemv_il_kernel<MT, FR, NWK, GV_ARGMAX><<<grid, NWK * 64, 0, st>>>(X, W, a);
+  const dim3 block(NWK * 64);
+  if (out == GV_PARTIAL) timed_launch(gemv_il_kernel<MT, FR, NWK, GV_PARTIAL>, grid, block, st, X, W, a);
+  else if (out == GV_RELU) timed_launch(gemv_il_kernel<MT, FR, NWK, GV_RELU>, grid, block, st, X, W, a);
+  else if (out == GV_QKV) timed_launch(gemv_il_kernel<MT, FR, NWK, GV_QKV>, grid, block, st, X, W, a);
+  else timed_launch(gemv_il_kernel<MT, FR, NWK, GV_ARGMAX>, grid, block, st, X, W, a);
 }
 
 template <int MT, int FR>

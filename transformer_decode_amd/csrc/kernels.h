@@ -10,6 +10,15 @@ namespace he {
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
 
+// Kernel timing for the runtime's per-class timers: when `start` is set, the next
+// launch of a decode GEMM or decode attention kernel is issued with
+// hipExtLaunchKernel and these events, which take their timestamps as part of that
+// dispatch (no separate event packets around it), and the pair is cleared.
+struct LaunchTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchTimer g_launch_timer;
+
 // ---- weight layout -------------------------------------------------------------
 // Inference layout of a bf16 weight with K columns (common.h, il_off): block width
 // 2^il_of(K) (the largest power of two <= 512 dividing K).
