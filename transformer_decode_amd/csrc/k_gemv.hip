@@ -74,13 +74,26 @@ GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole) 
     }
     return false;
   };
-  if (whole) {   // one group: the most rows per wave, the fewest waves per WG (1, 2, 4)
-                 // that put >= 512 waves in flight, a K range of K / nwk each
-    const long rg = (nrb + frmax - 1) / frmax;
+  if (whole) {   // one group, a K range of K / nwk per wave
+    auto rows = [&](int fr) { return (long)(nrb + fr - 1) / fr; };
+    if (rows(frmax) >= 512) {         // enough single-wave WGs (the LM head)
+      p.fr = frmax; p.nwk = 1; p.kr = K; p.splits = 1;
+      return p;
+    }
+    // few row groups (QKV): fill the 256 CUs evenly -- the fewest rounds of 256 WGs
+    // times rows per wave, ties to more rows per wave (3 rows per wave fits 768 row
+    // blocks to 256 WGs exactly) -- with waves per WG up to 4 toward 1024 waves
+    int best_fr = frmax;
+    long best_cost = -1;
+    for (int fr : {4, 3, 2, 1}) {
+      if (fr > frmax || (fr == 3 && p.mt > 4)) continue;
+      const long cost = (rows(fr) + 255) / 256 * fr;
+      if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_fr = fr; }
+    }
     int nwk = 1;
-    while (nwk < 4 && rg * nwk < 512 && K % (128 * nwk * 2) == 0) nwk *= 2;
+    while (nwk < 4 && rows(best_fr) * nwk < 1024 && K % (128 * nwk * 2) == 0) nwk *= 2;
     if (K % (128 * nwk) == 0) {
-      p.fr = frmax; p.nwk = nwk; p.kr = K / nwk; p.splits = 1;
+      p.fr = best_fr; p.nwk = nwk; p.kr = K / nwk; p.splits = 1;
       return p;
     }
   }
@@ -306,6 +319,7 @@ template <int MT>
 static void il_launch_fr(int out, const bf16* X, const bf16* W, const IlArgs& a, const GemvPlan& p,
                          hipStream_t st) {
   if (p.fr == 4 && MT <= 4) il_launch_nwk<MT, (MT <= 4 ? 4 : 2)>(out, X, W, a, p, st);
+  else if (p.fr == 3 && MT <= 4) il_launch_nwk<MT, (MT <= 4 ? 3 : 2)>(out, X, W, a, p, st);
   else if (p.fr >= 2) il_launch_nwk<MT, 2>(out, X, W, a, p, st);
   else il_launch_nwk<MT, 1>(out, X, W, a, p, st);
 }
