@@ -238,3 +238,26 @@ def test_opt125m_unfused_base_weights(c2_inputs):
     S = C2.prompt_len
     for j in steps:
         check_logits(got[j], full[:, S - 1 + j], C2.actor, f"unfused step {j}")
+
+
+def test_opt125m_ragged_prompt_pass(c2_inputs):
+    """A prompt pass whose B*S is a multiple of neither 16 nor 256 (3 x 37 = 111 rows):
+    the projections run the small-tile GEMM on activations in the inference layout with
+    a partial last 16-row block; then two decode steps at batch 3."""
+    params, lora, prompts, forced = c2_inputs
+    B, S = 3, 37
+    ids, fc = prompts[:B, :S].contiguous(), forced[:B].contiguous()
+    log("opt125m ragged prompt pass: GPU")
+    run = GpuRun(C2, params)
+    lt = run.lora(lora)
+    with torch.cuda.stream(run.stream):
+        he.he_fuse_lora(run.ctx, lt)
+        he.he_retake_cache(run.ctx, C2.batch, C2.max_seq)
+    got = run.teacher_forced(ids, fc, 3)
+    run.close()
+    log("opt125m ragged prompt pass: oracle")
+    om = _oracle(C2, params, lora)
+    seq = np.concatenate([ids.numpy(), fc.numpy()[:, :2]], axis=1)
+    full = om.forward_full(seq)
+    for j in range(3):
+        check_logits(got[j], full[:, S - 1 + j], C2.actor, f"ragged step {j}")

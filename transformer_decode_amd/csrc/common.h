@@ -105,6 +105,13 @@ __device__ __forceinline__ size_t xt_off(int m, int k, int mt) {
   return ((size_t)((k >> 5) * mt + (m >> 4)) << 9) + (((m & 15) | (((k >> 3) & 3) << 4)) << 3) + (k & 7);
 }
 
+// Activation layout code of a [M][K] storage-type matrix: 0 row-major; mt > 0 the
+// decode fragment tiling with mt row tiles (xt_off); -il < 0 the inference layout with
+// block width 2^il over K (il_off, as for weights), the prompt-pass GEMM operand.
+__device__ __forceinline__ size_t act_off(int m, int k, int K, int lay) {
+  return lay > 0 ? xt_off(m, k, lay) : il_off(m, k, K, -lay);
+}
+
 // Sum over the block in a fixed order (deterministic).  `red` holds >= nwaves floats.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;

@@ -216,6 +216,9 @@ static size_t parts_elems(he_ctx* c, int max_batch, int* argmax_cap) {
 
 // Layout of a layer weight with K columns as the kernels must read it now.
 static int w_il(const he_ctx* c, int K) { return (c->fused && c->dt == DT_BF16) ? il_of(K) : 0; }
+// Prompt-pass activations that feed a GEMM ([rows][K], bf16) are held in the inference
+// layout too: each 16 x 32 operand fragment is then 1 KB of whole cache lines.
+static int a_il(const he_ctx* c, int K) { return c->dt == DT_BF16 ? il_of(K) : 0; }
 static int e_il(const he_ctx* c) {
   return (c->fused && c->dt == DT_BF16 && c->desc.head == HE_HEAD_LM) ? c->il_d : 0;
 }
@@ -282,16 +285,16 @@ static void enqueue_prefill_lm(he_ctx* c, const int32_t* ids, int B, int S, bool
   const float eps = c->desc.ln_eps;
   const size_t es = esize(dt);
   hipStream_t st = c->stream;
-  const int ild = w_il(c, d), ilf = w_il(c, F);
+  const int ild = w_il(c, d), ilf = w_il(c, F), ald = a_il(c, d), alf = a_il(c, F);
   run_k(c, HE_K_EMBED_NORM, (double)M * d * (2 * es + 4 + es), 0, [&] {
     launch_embed_norm(dt, ids, nullptr, S, c->wt.tok_emb, c->wt.pos_emb,
                       c->L ? c->layers[0].ln1_g : c->wt.lnf_g, c->L ? c->layers[0].ln1_b : c->wt.lnf_b,
-                      eps, c->h, c->x, M, d, c->V, e_il(c), 0, st);
+                      eps, c->h, c->x, M, d, c->V, e_il(c), c->L ? -ald : 0, st);
   });
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
     EpiArgs e;
-    e.w_il = ild;
+    e.w_il = ild; e.x_il = ald;
     e.mode = EPI_QKV;
     e.bias = w.b_qkv;
     e.q_out = c->q;
@@ -301,27 +304,28 @@ static void enqueue_prefill_lm(he_ctx* c, const int32_t* ids, int B, int S, bool
     e.q_scale = c->q_scale;
     run_k(c, HE_K_GEMM_PREFILL, (double)3 * d * d * es, 2.0 * M * 3 * d * d,
           [&] { launch_gemm(dt, c->x, w.w_qkv, M, 3 * d, d, e, st); });
-    run_k(c, HE_K_ATTN_PREFILL, (double)M * d * es * 4, 2.0 * B * d * (double)S * (S + 1),
-          [&] { launch_attn_prefill(dt, c->q, kcache(c, l), vcache(c, l), c->o, B, S, c->H, c->D, c->max_seq, st); });
+    run_k(c, HE_K_ATTN_PREFILL, (double)M * d * es * 4, 2.0 * B * d * (double)S * (S + 1), [&] {
+      launch_attn_prefill(dt, c->q, kcache(c, l), vcache(c, l), c->o, B, S, c->H, c->D, c->max_seq, ald, st);
+    });
     EpiArgs r;
-    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h; r.w_il = ild;
+    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h; r.w_il = ild; r.x_il = ald;
     run_k(c, HE_K_GEMM_PREFILL, (double)d * d * es, 2.0 * M * d * d,
           [&] { launch_gemm(dt, c->o, w.w_out, M, d, d, r, st); });
     run_k(c, HE_K_EMBED_NORM, (double)M * d * (4 + es), 0, [&] {
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, 0, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, -ald, st);
     });
     EpiArgs f1;
-    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a; f1.w_il = ild;
+    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a; f1.w_il = ild; f1.x_il = ald; f1.o_il = alf;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
           [&] { launch_gemm(dt, c->x, w.w_fc1, M, F, d, f1, st); });
     EpiArgs f2;
-    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h; f2.w_il = ilf;
+    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h; f2.w_il = ilf; f2.x_il = alf;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
           [&] { launch_gemm(dt, c->a, w.w_fc2, M, d, F, f2, st); });
     if (l + 1 < c->L)
       run_k(c, HE_K_EMBED_NORM, (double)M * d * (4 + es), 0, [&] {
         launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[l + 1].ln1_g, c->layers[l + 1].ln1_b,
-                    eps, c->x, M, d, 1, 0, 0, 0, st);
+                    eps, c->x, M, d, 1, 0, 0, -ald, st);
       });
   }
   // final LayerNorm of the last prompt position only, laid out for the LM head
@@ -404,53 +408,60 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
   const size_t es = esize(dt);
   const bool post = c->desc.norm == HE_NORM_POST;
   hipStream_t st = c->stream;
+  // x feeds the first layer's QKV projection (inference layout), or with no layers the
+  // head (row-major)
+  const int ald = a_il(c, d), alf = a_il(c, F), x0 = c->L ? -ald : 0;
   if (de != d) {
     launch_embed_gather(dt, ids, c->wt.tok_emb, c->xe, M, de, c->V, st);
     EpiArgs e;
     e.mode = EPI_POSADD; e.pos_emb = c->wt.pos_emb; e.h = c->h; e.out = c->x; e.seq_len = S; e.pos0 = 0;
+    e.o_il = (post || !c->L) ? -x0 : 0;   // pre-LN: the norm below writes the GEMM input
     run_k(c, HE_K_GEMM_PREFILL, (double)d * de * es, 2.0 * M * d * de,
           [&] { launch_gemm(dt, c->xe, c->wt.proj_in, M, d, de, e, st); });
     if (!post && c->L)
       launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[0].ln1_g, c->layers[0].ln1_b, eps, c->x, M, d,
-                  1, 0, 0, 0, st);
+                  1, 0, 0, x0, st);
   } else {
     launch_embed_norm(dt, ids, nullptr, S, c->wt.tok_emb, c->wt.pos_emb,
                       (!post && c->L) ? c->layers[0].ln1_g : nullptr,
                       (!post && c->L) ? c->layers[0].ln1_b : nullptr, eps, c->h, c->x, M, d, c->V,
-                      e_il(c), 0, st);
+                      e_il(c), x0, st);
   }
   const int ild = w_il(c, d), ilf = w_il(c, F);
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
     EpiArgs e;
-    e.w_il = ild;
+    e.w_il = ild; e.x_il = ald;
     e.mode = EPI_QKV; e.bias = w.b_qkv; e.q_out = c->q; e.k_cache = kcache(c, l); e.v_cache = vcache(c, l);
     e.d = d; e.H = c->H; e.D = c->D; e.S_max = c->max_seq; e.seq_len = S; e.pos0 = 0; e.q_scale = c->q_scale;
     run_k(c, HE_K_GEMM_PREFILL, (double)3 * d * d * es, 2.0 * M * 3 * d * d,
           [&] { launch_gemm(dt, c->x, w.w_qkv, M, 3 * d, d, e, st); });
-    run_k(c, HE_K_ATTN_PREFILL, (double)M * d * es * 4, 2.0 * B * d * (double)S * (S + 1),
-          [&] { launch_attn_prefill(dt, c->q, kcache(c, l), vcache(c, l), c->o, B, S, c->H, c->D, c->max_seq, st); });
+    run_k(c, HE_K_ATTN_PREFILL, (double)M * d * es * 4, 2.0 * B * d * (double)S * (S + 1), [&] {
+      launch_attn_prefill(dt, c->q, kcache(c, l), vcache(c, l), c->o, B, S, c->H, c->D, c->max_seq, ald, st);
+    });
     EpiArgs r;
-    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h; r.w_il = ild;
+    r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h; r.w_il = ild; r.x_il = ald;
     run_k(c, HE_K_GEMM_PREFILL, (double)d * d * es, 2.0 * M * d * d,
           [&] { launch_gemm(dt, c->o, w.w_out, M, d, d, r, st); });
     if (post)
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln1_g, w.ln1_b, eps, c->x, M, d, 1, 0, 1, 0, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln1_g, w.ln1_b, eps, c->x, M, d, 1, 0, 1, -ald, st);
     else
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, 0, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, -ald, st);
     EpiArgs f1;
-    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a; f1.w_il = ild;
+    f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a; f1.w_il = ild; f1.x_il = ald; f1.o_il = alf;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
           [&] { launch_gemm(dt, c->x, w.w_fc1, M, F, d, f1, st); });
     EpiArgs f2;
-    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h; f2.w_il = ilf;
+    f2.mode = EPI_RESID; f2.bias = w.b_fc2; f2.h = c->h; f2.w_il = ilf; f2.x_il = alf;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
           [&] { launch_gemm(dt, c->a, w.w_fc2, M, d, F, f2, st); });
+    // post-LN: the last layer's output goes to the head, which reads x row-major
     if (post)
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 1, 0, st);
+      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 1,
+                  l + 1 < c->L ? -ald : 0, st);
     else if (l + 1 < c->L)
       launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[l + 1].ln1_g, c->layers[l + 1].ln1_b, eps, c->x,
-                  M, d, 1, 0, 0, 0, st);
+                  M, d, 1, 0, 0, -ald, st);
   }
   int xs = S;
   if (!post) {   // pre-LN: final LayerNorm of the last position
@@ -656,7 +667,8 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   }
   const size_t es = esize(c->dt);
   const int bpad = c->dt == DT_BF16 ? 16 * decode_mt(max_batch) : round_up(max_batch, 16);
-  const size_t rows = std::max<size_t>((size_t)max_batch * max_seq, (size_t)bpad);
+  // rows rounded to 16: the inference layout of an activation fills whole 16-row blocks
+  const size_t rows = (std::max<size_t>((size_t)max_batch * max_seq, (size_t)bpad) + 15) / 16 * 16;
   const size_t kv_layer = (size_t)max_batch * c->H * max_seq * c->D;
   const size_t kv_bytes = kv_layer * 2 * c->L * es;
   // scratch layout (256-byte aligned pieces)

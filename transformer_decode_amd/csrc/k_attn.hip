@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16* __re
                                                                 const bf16* __restrict__ kc,
                                                                 const bf16* __restrict__ vc,
                                                                 bf16* __restrict__ o, int B,
-                                                                int S, int H, int S_max) {
+                                                                int S, int H, int S_max, int o_il) {
   constexpr int KT = 64;                 // keys per tile
   constexpr int LDKS = D + 8;            // K tile row stride (bf16)
   constexpr int LDV = KT + 8;            // transposed V row stride
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16* __re
     const float inv = 1.f / l_r[r];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-      o[((size_t)b * S + qi) * d + h * D + t * 16 + fr] = f2bf(oacc[t][r] * inv);
+      o[il_off(b * S + qi, h * D + t * 16 + fr, d, o_il)] = f2bf(oacc[t][r] * inv);
   }
 }
 
@@ -446,18 +446,18 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __res
 }
 
 void launch_attn_prefill(int dt, const void* q, const void* k_cache, const void* v_cache, void* o,
-                         int B, int S, int H, int D, int S_max, hipStream_t st) {
+                         int B, int S, int H, int D, int S_max, int o_il, hipStream_t st) {
   if (dt == DT_BF16) {
     dim3 grid((S + 63) / 64, B * H);
     if (D == 64)
       attn_prefill_bf16_kernel<64><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
-                                                         (const bf16*)v_cache, (bf16*)o, B, S, H, S_max);
+                                                         (const bf16*)v_cache, (bf16*)o, B, S, H, S_max, o_il);
     else if (D == 128)
       attn_prefill_bf16_kernel<128><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
-                                                          (const bf16*)v_cache, (bf16*)o, B, S, H, S_max);
+                                                          (const bf16*)v_cache, (bf16*)o, B, S, H, S_max, o_il);
     else
       attn_prefill_bf16_kernel<32><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
-                                                         (const bf16*)v_cache, (bf16*)o, B, S, H, S_max);
+                                                         (const bf16*)v_cache, (bf16*)o, B, S, H, S_max, o_il);
   } else {
     dim3 grid(S, B * H);
     size_t lds = (size_t)(D + S) * sizeof(float);

@@ -204,10 +204,11 @@ __device__ __forceinline__ void st4(bf16* p, const float* v) {
   *reinterpret_cast<uint2*>(p) = u;
 }
 
-// x row `row` of the GEMM input: row-major [.][d], or fragment-tiled (x_mt tiles).
+// x row `row` of the GEMM input in layout x_lay (act_off): row-major [.][d], decode
+// fragment tiles, or the inference layout.
 template <typename T>
-__device__ __forceinline__ T* x_at(T* x, int row, int k, int d, int x_mt) {
-  return x + (x_mt ? xt_off(row, k, x_mt) : (size_t)row * d + k);
+__device__ __forceinline__ T* x_at(T* x, int row, int k, int d, int x_lay) {
+  return x + act_off(row, k, d, x_lay);
 }
 
 // LayerNorm of one row held by the block (up to kLnChunks chunks of 4 per thread),
@@ -216,7 +217,7 @@ __device__ __forceinline__ T* x_at(T* x, int row, int k, int d, int x_mt) {
 // fetched before the reductions so their latency overlaps them.
 template <typename T>
 __device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, float eps,
-                                         const T* g, const T* b, T* x, int row, int x_mt,
+                                         const T* g, const T* b, T* x, int row, int x_lay,
                                          float* hrow_post, float* red) {
   const int tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   float gv[kLnChunks][4], bv[kLnChunks][4];
@@ -246,7 +247,7 @@ __device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, 
 #pragma unroll
       for (int q = 0; q < 4; ++q) y[q] = (v[c][q] - mean) * rstd * gv[c][q] + bv[c][q];
       if (hrow_post) st4(hrow_post + ch * 4, y);   // post-LN: the stream is the norm
-      st4(x_at(x, row, ch * 4, d, x_mt), y);         // GEMM input: rounded
+      st4(x_at(x, row, ch * 4, d, x_lay), y);         // GEMM input: rounded
     }
   }
 }
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* __restr
                                                           const T* __restrict__ g,
                                                           const T* __restrict__ b, float eps,
                                                           float* __restrict__ h, T* __restrict__ x,
-                                                          int d, int vocab, int e_il, int x_mt) {
+                                                          int d, int vocab, int e_il, int x_lay) {
   __shared__ float red[64];
   const int m = blockIdx.x, tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   int id = ids[m];
@@ -289,24 +290,24 @@ __global__ __launch_bounds__(1024) void embed_norm_kernel(const int32_t* __restr
     }
   }
   if (g) {
-    ln_write<T>(v, d, eps, g, b, x, m, x_mt, nullptr, red);
+    ln_write<T>(v, d, eps, g, b, x, m, x_lay, nullptr, red);
   } else {
 #pragma unroll
     for (int c = 0; c < kLnChunks; ++c) {
       const int ch = tid + c * nt;
-      if (ch < nch) st4(x_at(x, m, ch * 4, d, x_mt), v[c]);
+      if (ch < nch) st4(x_at(x, m, ch * 4, d, x_lay), v[c]);
     }
   }
 }
 
 void launch_embed_norm(int dt, const int32_t* ids, const int32_t* pos_dev, int seq_len,
                        const void* E, const void* P, const void* g, const void* b, float eps,
-                       float* h, void* x, int M, int d, int vocab, int e_il, int x_mt, hipStream_t st) {
+                       float* h, void* x, int M, int d, int vocab, int e_il, int x_lay, hipStream_t st) {
   const int nt = ln_threads(d);
   if (dt == DT_BF16)
     embed_norm_kernel<bf16><<<M, nt, 0, st>>>(ids, pos_dev, seq_len, (const bf16*)E, (const bf16*)P,
                                               (const bf16*)g, (const bf16*)b, eps, h, (bf16*)x, d, vocab,
-                                              e_il, x_mt);
+                                              e_il, x_lay);
   else
     embed_norm_kernel<float><<<M, nt, 0, st>>>(ids, pos_dev, seq_len, (const float*)E, (const float*)P,
                                                (const float*)g, (const float*)b, eps, h, (float*)x, d, vocab,
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
                                                     const T* __restrict__ g,
                                                     const T* __restrict__ b, float eps,
                                                     T* __restrict__ x, int M, int d, int row_stride,
-                                                    int row_offset, int post, int x_mt) {
+                                                    int row_offset, int post, int x_lay) {
   __shared__ float red[64];
   const int r = blockIdx.x, tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   const size_t row = (size_t)r * row_stride + row_offset;
@@ -382,17 +383,17 @@ __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
       }
     }
   }
-  ln_write<T>(v, d, eps, g, b, x, r, x_mt, post ? hr : nullptr, red);
+  ln_write<T>(v, d, eps, g, b, x, r, x_lay, post ? hr : nullptr, red);
 }
 
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias, const void* g,
                  const void* b, float eps, void* x, int M, int d, int row_stride, int row_offset,
-                 int post, int x_mt, hipStream_t st) {
+                 int post, int x_lay, hipStream_t st) {
   const int nt = ln_threads(d);
   if (dt == DT_BF16)
     norm_kernel<bf16><<<M, nt, 0, st>>>(h, parts, nsplit, (const bf16*)bias, (const bf16*)g,
                                         (const bf16*)b, eps, (bf16*)x, M, d, row_stride, row_offset, post,
-                                        x_mt);
+                                        x_lay);
   else
     norm_kernel<float><<<M, nt, 0, st>>>(h, parts, nsplit, (const float*)bias, (const float*)g,
                                          (const float*)b, eps, (float*)x, M, d, row_stride, row_offset, post,

@@ -1,12 +1,14 @@
 // Prompt-pass projections of libhe: Y[M,N] = X[M,K] W[N,K]^T with fused epilogues.
 //
-// bf16 models: MFMA (v_mfma_f32_16x16x32_bf16) GEMM with 128 x 128 macro tiles,
-// BK = 32, LDS double buffering; four waves each own a 64 x 64 sub-tile (4 x 4
-// MFMA tiles).  fp32 models (the tiny workload only): a plain tiled FMA kernel.
-// Both end in the same epilogue: bias, q scaling + KV-cache scatter (the prompt's
-// keys and values enter the cache here), residual add, ReLU, position add.  bf16
-// weights are read row-major or in the inference layout (EpiArgs::w_il, il_off):
-// a 16-byte chunk is 8 consecutive k of one row in both.
+// bf16 models: for M, N multiples of 256 an MFMA GEMM on 32 x 32 x 16 tiles with
+// 256 x 256 macro tiles staged by LDS DMA (gemm_frag_kernel); other shapes run a
+// 256 x 256 (8 waves) or 128 x 128 (4 waves) kernel on 16 x 16 x 32 tiles with
+// register-staged loads.  fp32 models (the tiny workload only): a plain tiled FMA
+// kernel.  All end in the same epilogue: bias, q scaling + KV-cache scatter (the
+// prompt's keys and values enter the cache here), residual add, ReLU, position add.
+// bf16 weights and activations are read row-major or in the inference layout
+// (EpiArgs::w_il / x_il, il_off), and ReLU / position-add outputs written in either
+// (o_il): a 16-byte chunk is 8 consecutive k of one row in both.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,12 +35,12 @@ __device__ __forceinline__ void epi_store(const EpiArgs& e, int m, int n, int N,
     e.h[(size_t)m * N + n] += acc + bv;
   } else if (MODE == EPI_RELU) {
     float v = acc + ld((const T*)e.bias + n);
-    st((T*)e.out + (size_t)m * N + n, fmaxf(v, 0.f));
+    st((T*)e.out + il_off(m, n, N, e.o_il), fmaxf(v, 0.f));
   } else if (MODE == EPI_POSADD) {
     const int t = m % e.seq_len;
     float v = acc + ld((const T*)e.pos_emb + (size_t)(e.pos0 + t + 2) * N + n);
     e.h[(size_t)m * N + n] = v;
-    st((T*)e.out + (size_t)m * N + n, v);
+    st((T*)e.out + il_off(m, n, N, e.o_il), v);
   } else {
     float bv = e.bias ? ld((const T*)e.bias + n) : 0.f;
     e.out_f32[(size_t)m * N + n] = acc + bv;
@@ -85,7 +87,7 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, int m, int n, int N
   } else if (MODE == EPI_RELU) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] = fmaxf(acc[c] + b[c], 0.f);
-    st_bf4((bf16*)e.out + (size_t)m * N + n, v);
+    st_bf4((bf16*)e.out + il_off(m, n, N, e.o_il), v);
   } else if (MODE == EPI_POSADD) {
     const int t = m % e.seq_len;
     float p[4];
@@ -93,10 +95,55 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, int m, int n, int N
 #pragma unroll
     for (int c = 0; c < 4; ++c) v[c] = acc[c] + p[c];
     *reinterpret_cast<float4*>(e.h + (size_t)m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
-    st_bf4((bf16*)e.out + (size_t)m * N + n, v);
+    st_bf4((bf16*)e.out + il_off(m, n, N, e.o_il), v);
   } else {
     *reinterpret_cast<float4*>(e.out_f32 + (size_t)m * N + n) =
         make_float4(acc[0] + b[0], acc[1] + b[1], acc[2] + b[2], acc[3] + b[3]);
+  }
+}
+
+// Eight consecutive output columns n .. n + 7 of row m (bf16 storage, n % 8 == 0).
+template <int MODE>
+__device__ __forceinline__ void epi_store8(const EpiArgs& e, int m, int n, int N, const float (&acc)[8]) {
+  float b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, v[8];
+  if (MODE != EPI_POSADD && e.bias) load8((const bf16*)e.bias + n, b);
+  if (MODE == EPI_QKV) {
+    const int part = n / e.d, within = n - part * e.d;
+    const int head = within / e.D, dd = within - head * e.D;
+    const int bb = m / e.seq_len, t = m - bb * e.seq_len;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = acc[c] + b[c];
+    if (part == 0) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] *= e.q_scale;
+      store8((bf16*)e.q_out + (size_t)m * e.d + within, v);
+    } else {
+      bf16* cache = (bf16*)(part == 1 ? e.k_cache : e.v_cache);
+      store8(cache + (((size_t)bb * e.H + head) * e.S_max + e.pos0 + t) * e.D + dd, v);
+    }
+  } else if (MODE == EPI_RESID) {
+    float* hp = e.h + (size_t)m * N + n;
+    float h[8];
+    load8(hp, h);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) h[c] += acc[c] + b[c];
+    store8(hp, h);
+  } else if (MODE == EPI_RELU) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = fmaxf(acc[c] + b[c], 0.f);
+    store8((bf16*)e.out + il_off(m, n, N, e.o_il), v);
+  } else if (MODE == EPI_POSADD) {
+    const int t = m % e.seq_len;
+    float p[8];
+    load8((const bf16*)e.pos_emb + (size_t)(e.pos0 + t + 2) * N + n, p);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = acc[c] + p[c];
+    store8(e.h + (size_t)m * N + n, v);
+    store8((bf16*)e.out + il_off(m, n, N, e.o_il), v);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = acc[c] + b[c];
+    store8(e.out_f32 + (size_t)m * N + n, v);
   }
 }
 
@@ -124,7 +171,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16* __restrict__
     for (int i = 0; i < 2; ++i) {
       const int r = lr + 64 * i;
       const int gm = m0 + r, gn = n0 + r;
-      ra[i] = (gm < M && k < K) ? *reinterpret_cast<const uint4*>(X + (size_t)gm * K + k)
+      ra[i] = (gm < M && k < K) ? *reinterpret_cast<const uint4*>(X + il_off(gm, k, K, e.x_il))
                                 : make_uint4(0, 0, 0, 0);
       rb[i] = (gn < N && k < K) ? *reinterpret_cast<const uint4*>(W + il_off(gn, k, K, e.w_il))
                                 : make_uint4(0, 0, 0, 0);
@@ -222,7 +269,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(const bf16* __restri
       const int id = tid + i * 512, r = id >> 3, c = id & 7;
       const int k = kt * LBK + c * 8;
       const int gm = m0 + r, gn = n0 + r;
-      ra[i] = (gm < M && k < K) ? *reinterpret_cast<const uint4*>(X + (size_t)gm * K + k) : make_uint4(0, 0, 0, 0);
+      ra[i] = (gm < M && k < K) ? *reinterpret_cast<const uint4*>(X + il_off(gm, k, K, e.x_il)) : make_uint4(0, 0, 0, 0);
       rb[i] = (gn < N && k < K) ? *reinterpret_cast<const uint4*>(W + il_off(gn, k, K, e.w_il)) : make_uint4(0, 0, 0, 0);
     }
   };
@@ -284,21 +331,34 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(const bf16* __restri
 // bf16 MFMA GEMM on 32 x 32 x 16 tiles staged by LDS DMA (M, N multiples of 256,
 // K of 32).  256 x 256 macro tile, 4 waves (2 x 2), each owning 128 x 128 as 4 x 4
 // v_mfma_f32_32x32x16_bf16 tiles (accumulators in AGPRs).  With one wave per SIMD
-// this instruction sustains about 2.1 PFLOP/s where the 16 x 16 x 32 one stops
-// near 1.3 (measured).  An operand fragment is 32 rows x 16 k = 1 KB, lane l holding
-// row l % 32, k 8 (l / 32) .. + 8.  A stage is 32 k: 16 fragments of X and 16 of W.
-// Waves fill LDS with global_load_lds_dwordx4, each lane fetching its own 16 bytes
-// (8 consecutive k of one row in row-major X and in either layout of W, il_off) to
-// slot + 16 l, so operands come back with conflict-free ds_read_b128 and never pass
-// through VGPRs on the way in.  Four stages (128 KB of LDS) rotate: loads run three
-// stages ahead of the MFMAs.
+// this instruction sustains about 2.1 PFLOP/s on constant operands (1.65 to 1.7 on
+// random ones, where power sets the clock) where the 16 x 16 x 32 one stops near 1.3
+// (measured).  An operand fragment is 32 rows x 16 k = 1 KB, lane l holding row
+// l % 32, k 8 (l / 32) .. + 8.  A stage is 32 k, staged as 16 fragments of X and 16
+// of W in the 16 x 32 shape of the weights' inference layout (1 KB each, lane l at
+// row l % 16, k 8 (l / 16)), filled with buffer_load_dwordx4 ... lds: each lane's 16
+// bytes (8 consecutive k of one row) land at slot + 16 l.  A W fragment in the
+// inference layout is 1 KB of consecutive bytes (whole cache lines); row-major X is
+// 16 rows x 64 bytes.  The 32 x 32 x 16 operands are read back from pairs of
+// fragments with ds_read_b128 free of bank conflicts, and never pass through VGPRs
+// on the way in.  Four stages (128 KB of LDS) rotate: loads run three stages ahead
+// of the MFMAs.
 // ---------------------------------------------------------------------------------
 constexpr int FBM = 256, FBN = 256, FST = 4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ void lds_dma16(const void* g, bf16* lds_slot) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_slot, 16, 0, 0);
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 descriptor word 3: 32-bit
+// data format, no swizzle), for buffer_load_dwordx4 ... lds.  The buffer form of the
+// LDS DMA takes a scalar offset per access and one VGPR per lane, and unlike the
+// global_load_lds form it is not taken by the compiler for a possible out-of-order LDS
+// access, so its LDS reads keep precise lgkmcnt waits.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r, bf16* lds_slot, uint32_t voff,
+                                          uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_slot, 16, voff, soff, 0, 0);
 }
 
 // s_waitcnt with vmcnt = n (n < 64), expcnt and lgkmcnt left open (gfx9 encoding).
@@ -310,7 +370,25 @@ __device__ __forceinline__ void lds_dma16(const void* g, bf16* lds_slot) {
 // compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int MODE, bool WIL>
+// Offsets of the 16 x 32 fragment (16-row tile, k-step s) of a [rows][K] operand in
+// layout il (0 row-major, else the inference layout, il_off).  The address of lane l
+// splits into a part fixed for the kernel and a wave-uniform part per k-step.  Row-major:
+// row l % 16, k 8 (l / 16) + 32 s (16 rows x 64 bytes).  Inference layout with block
+// width BW = 2^il: the fragment is 512 / BW row pieces of BW / 8 units (1 KB of
+// consecutive bytes for BW = 512): lane part (l / (BW / 8)) K + 8 (l mod BW / 8), k-step
+// part the block row and column of k 32 s (il_frag).
+__device__ __forceinline__ uint32_t frag_lane_part(int lane, int K, int il) {
+  if (il == 0) return (uint32_t)((lane & 15) * K + ((lane >> 4) << 3));
+  const int lgu = il - 3;
+  return (uint32_t)((lane >> lgu) * K + ((lane & ((1 << lgu) - 1)) << 3));
+}
+__device__ __forceinline__ uint32_t frag_step_part(int s, int K, int il) {
+  if (il == 0) return (uint32_t)(32 * s);
+  const int q = s & ((1 << (il - 5)) - 1);
+  return (uint32_t)(((q << 6) >> (il - 3)) * K + ((s >> (il - 5)) << il));
+}
+
+template <int MODE, bool WIL, bool XIL>
 __global__ __launch_bounds__(256) void gemm_frag_kernel(const bf16* __restrict__ X,
                                                         const bf16* __restrict__ W, int M, int N,
                                                         int K, EpiArgs e) {
@@ -330,46 +408,37 @@ __global__ __launch_bounds__(256) void gemm_frag_kernel(const bf16* __restrict__
   const int gsz = min(nm - first_m, GM);
   const int tm = first_m + (t % (GM * nn)) % gsz, tn = (t % (GM * nn)) / gsz;
   const int m0 = tm * FBM, n0 = tn * FBN;
-  // Stage s (k 32 s .. + 32): this wave loads fragments f = 4 wv + q (q < 4) of each
-  // operand.  Every lane's 16 bytes are 8 consecutive k of one row, at an address
-  // that splits into a per-lane offset fixed for the kernel plus a wave-uniform
-  // offset per stage.  Row-major: row * K + 16 ks + 8 (l / 32) per lane, 32 s
-  // uniform.  Inference layout (il_off) with block width BW = 2^il: stage s sits
-  // at k-in-block kb = 32 s mod BW, which moves every unit of the fragment by
-  // (kb / 32) * 64 positions = (kb / 32) * 64 / (BW / 8) block rows, plus the
-  // block's column offset 32 s - kb.
-  const int lrow = lane & 31, lk = (lane >> 5) << 3;
-  uint32_t offa[4], offb[4];
+  // Stage s (k 32 s .. + 32) holds each operand as 16 fragments of 16 rows x 32 k
+  // (1 KB, lane l at row l % 16, k 8 (l / 16) .. + 8); this wave loads fragments
+  // 4 wv .. 4 wv + 3 of each.
+  const int ilx = XIL ? e.x_il : 0, ilw = WIL ? e.w_il : 0;
+  // One buffer resource per operand over this tile's 256 rows (byte offsets within a
+  // tile stay far below 2^32: 256 K 2 bytes).
+  const uint32_t tile_bytes = (uint32_t)(FBM * K * 2);
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(X + (size_t)m0 * K, tile_bytes);
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W + (size_t)n0 * K, tile_bytes);
+  // Byte offsets: per lane (lane part plus the row offset of each of this wave's four
+  // 16-row tiles, fixed for the kernel) and per stage (one scalar per operand).
+  const uint32_t lane_x = frag_lane_part(lane, K, ilx), lane_w = frag_lane_part(lane, K, ilw);
+  uint32_t vx[4], vw[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int f = wv * 4 + q, ks = f >> 3, tile = f & 7;
-    offa[q] = (uint32_t)((tile * 32 + lrow) * K + ks * 16 + lk);
-    if (WIL) {
-      const int il = e.w_il, lgu = il - 3;
-      const int j = lrow & 15, u = 2 * ks + (lane >> 5);            // unit within the 32-k step
-      const int pl = (u << 4) | j;                                   // position for kb = 0
-      offb[q] = (uint32_t)((tile * 32 + (lrow & 16) + (pl >> lgu)) * K + ((pl & ((1 << lgu) - 1)) << 3));
-    } else {
-      offb[q] = offa[q];
-    }
+    const uint32_t rows = (uint32_t)((wv * 4 + q) * 16 * K);
+    vx[q] = (lane_x + rows) * 2;
+    vw[q] = (lane_w + rows) * 2;
   }
-  const long ua0 = (long)m0 * K, ub0 = (long)n0 * K;
-  auto issue = [&](int s) {
-    bf16* sa = fsm + (size_t)(s & (FST - 1)) * 2 * 16 * 512;
-    bf16* sb = sa + 16 * 512;
-    long ub = ub0 + 32L * s;
-    if (WIL) {
-      const int il = e.w_il, lgu = il - 3, kb = (32 * s) & ((1 << il) - 1);
-      ub = ub0 + (long)(((kb >> 5) << 6) >> lgu) * K + (32L * s - kb);
-    }
-    const bf16* xa = X + ua0 + 32L * s;
-    const bf16* wb = W + ub;
+  // DMA g (0..7) of k-step s into stage buffer buf: 16-row tile 4 wv + g / 2 of X
+  // (g even) or W (g odd)
+  auto dma = [&](int g, int s, int buf) {
+    bf16* sa = fsm + (size_t)buf * 2 * 16 * 512 + (wv * 4 + (g >> 1)) * 512;
+    if ((g & 1) == 0)
+      buf_dma16(rx, sa, vx[g >> 1], frag_step_part(s, K, ilx) * 2);
+    else
+      buf_dma16(rw, sa + 16 * 512, vw[g >> 1], frag_step_part(s, K, ilw) * 2);
+  };
+  auto issue = [&](int s, int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int f = wv * 4 + q;
-      lds_dma16(xa + offa[q], sa + f * 512);
-      lds_dma16(wb + offb[q], sb + f * 512);
-    }
+    for (int g = 0; g < 8; ++g) dma(g, s, buf);
   };
 
   f32x16 acc[4][4];
@@ -380,14 +449,22 @@ __global__ __launch_bounds__(256) void gemm_frag_kernel(const bf16* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // operands of one 16-wide k-step: b[0..3] then a[0..3] (wave tile columns, rows)
+  // Operands of one 16-wide k-step ks of a stage: b[0..3] then a[0..3] (wave tile
+  // columns, rows).  The 32 x 32 x 16 operand (lane l: row l % 32, k 8 (l / 32) .. + 8
+  // of the step) of 32-row tile t is gathered from the 16-row fragments 2t and 2t + 1:
+  // row r sits in fragment 2t + r / 16 at lane (r mod 16) + 16 (2 ks + l / 32).  Each
+  // 16 lanes read 256 consecutive bytes, so the reads are free of bank conflicts.
+  const int rl = lane & 31;
+  const uint32_t lane_lds = (uint32_t)((rl >> 4) * 512 + ((rl & 15) + ((lane >> 5) << 4)) * 8);
+  // operand g of k-step ks of stage s: g < 4 column tile g of W, else row tile g - 4 of X
+  auto read_frag = [&](int s, int ks, int g) -> bf16x8 {
+    const bf16* sa = fsm + (size_t)(s & (FST - 1)) * 2 * 16 * 512 + ks * 256 + lane_lds;
+    return g < 4 ? *reinterpret_cast<const bf16x8*>(sa + 16 * 512 + (wn * 4 + g) * 1024)
+                 : *reinterpret_cast<const bf16x8*>(sa + (wm * 4 + g - 4) * 1024);
+  };
   auto read_frags = [&](int s, int ks, bf16x8 (&r)[8]) {
-    const bf16* sa = fsm + (size_t)(s & (FST - 1)) * 2 * 16 * 512;
-    const bf16* sb = sa + 16 * 512;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const bf16x8*>(sb + (ks * 8 + wn * 4 + j) * 512 + lane * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[4 + i] = *reinterpret_cast<const bf16x8*>(sa + (ks * 8 + wm * 4 + i) * 512 + lane * 8);
+    for (int g = 0; g < 8; ++g) r[g] = read_frag(s, ks, g);
   };
   auto mma = [&](const bf16x8 (&r)[8]) {
 #pragma unroll
@@ -397,59 +474,82 @@ __global__ __launch_bounds__(256) void gemm_frag_kernel(const bf16* __restrict__
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[j], r[4 + i], acc[i][j], 0, 0, 0);
   };
 
-  // With one wave per SIMD, instructions issue in order: the LDS reads of the next
-  // k-step are spread between the MFMAs (scheduling groups) rather than queued in
-  // front of them.  r0 holds the first 16-wide k-step of a stage, r1 the second;
-  // each is read one half-stage before its MFMAs.  The loop body is straight-line
-  // (the last stage re-reads its own first k-step instead of a next one) so the
-  // accumulators stay in place.
+  // With one wave per SIMD, instructions issue in order: the DMA issues and the LDS
+  // reads of the next k-step are spread between the MFMAs (scheduling groups) rather
+  // than queued in front of them.  r0 holds the first 16-wide k-step of a stage, r1
+  // the second; each is read one half-stage before its MFMAs.  The loop body is
+  // straight-line so the accumulators stay in place: every iteration issues one
+  // stage of DMA (the last FST - 1 repeat the final stage's addresses into the free
+  // buffer, which is never read again) and the last stage re-reads its own first
+  // k-step instead of a next one.
   const int ns = K / 32;
 #pragma unroll
-  for (int s = 0; s < FST - 1; ++s)
-    if (s < ns) issue(s);
+  for (int s = 0; s < FST - 1; ++s) issue(min(s, ns - 1), s);
   HE_WAIT_VMCNT(8 * (FST - 2));
   barrier_keep_loads();
   bf16x8 r0[8], r1[8];
   read_frags(0, 0, r0);
+  // group g of a half-stage: MFMAs (row tile g / 2, column tiles 2 (g % 2) + 0, 1)
+  auto mma2 = [&](const bf16x8 (&r)[8], int g) {
+    const int i = g >> 1, j = (g & 1) << 1;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[j], r[4 + i], acc[i][j], 0, 0, 0);
+    acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[j + 1], r[4 + i], acc[i][j + 1], 0, 0, 0);
+  };
   for (int s = 0; s < ns; ++s) {
-    // refill the stage that s - 1 used (every wave read it before the last barrier)
-    const bool refill = s + FST - 1 < ns;
-    if (refill) issue(s + FST - 1);
-    read_frags(s, 1, r1);
-    mma(r0);
+    // half A: refill the buffer that stage s - 1 used (every wave read it before the
+    // last barrier), read the second k-step of stage s, multiply the first; each group
+    // is one DMA issue, one LDS read and two MFMAs, in that order
+    const int sd = min(s + FST - 1, ns - 1), bd = (s + FST - 1) & (FST - 1);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+      dma(g, sd, bd);
+      r1[g] = read_frag(s, 1, g);
+      mma2(r0, g);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // stage s + 1 must have landed here and in every wave before it is read
-    if (refill) HE_WAIT_VMCNT(8 * (FST - 2));
-    else HE_WAIT_VMCNT(0);
+    HE_WAIT_VMCNT(8 * (FST - 2));
     barrier_keep_loads();
-    read_frags(s + 1 < ns ? s + 1 : s, 0, r0);
-    mma(r1);
+    // half B: read the first k-step of stage s + 1, multiply the second of stage s
+    const int sn = s + 1 < ns ? s + 1 : s;
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+      r0[g] = read_frag(sn, 0, g);
+      mma2(r1, g);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  HE_WAIT_VMCNT(0);     // the repeated tail stages land before LDS is reused below
+  barrier_keep_loads();
 
-  // Epilogue straight from the accumulators.  The MFMAs compute W X^T per tile (W
-  // fragment as the first operand), so lane l holds output row m = l % 32 of the
-  // tile and register 4 q + c holds column n = 8 q + 4 (l / 32) + c: four
-  // consecutive columns per register quad, stored with one vector access.
+  // Epilogue through LDS (free after the last barrier), a quarter of the wave tile at
+  // a time: the MFMAs compute W X^T per tile, so lane l holds output row l % 32 and
+  // register 4 q + c holds column 8 q + 4 (l / 32) + c; each wave parks 32 rows x 128
+  // columns (fp32, rows padded to 132 words: conflict-free 16-byte writes) in its own
+  // region, then reads them back as 8 consecutive columns per lane, so 16 lanes cover
+  // a row and every store is a 16- or 32-byte access to whole row segments.
+  constexpr int PR = 132;
+  float* park = reinterpret_cast<float*>(fsm) + (size_t)wv * 32 * PR;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 128 + i * 32 + lrow;
-        const int n = n0 + wn * 128 + j * 32 + q * 8 + ((lane >> 5) << 2);
-        const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        epi_store4<MODE>(e, m, n, N, v);
-      }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(park + rl * PR + j * 32 + q * 8 + ((lane >> 5) << 2)) =
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    __builtin_amdgcn_s_waitcnt(0);   // lgkmcnt(0): this wave's parked rows are in LDS
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int seg = lane + it * 64, row = seg >> 4, col = (seg & 15) << 3;
+      float v[8];
+      const float4 v0 = *reinterpret_cast<const float4*>(park + row * PR + col);
+      const float4 v1 = *reinterpret_cast<const float4*>(park + row * PR + col + 4);
+      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      epi_store8<MODE>(e, m0 + wm * 128 + i * 32 + row, n0 + wn * 128 + col, N, v);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // reads done before the next quarter overwrites
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -497,10 +597,15 @@ static void gemm_dispatch(int dt, const void* X, const void* W, int M, int N, in
   if (dt == DT_BF16) {
     if (M % FBM == 0 && N % FBN == 0 && K % 32 == 0) {
       const int blocks = ((M / FBM) * (N / FBN) + 7) / 8 * 8;
-      if (e.w_il)
-        gemm_frag_kernel<MODE, true><<<blocks, 256, 0, st>>>((const bf16*)X, (const bf16*)W, M, N, K, e);
+      const bf16 *x = (const bf16*)X, *w = (const bf16*)W;
+      if (e.w_il && e.x_il)
+        gemm_frag_kernel<MODE, true, true><<<blocks, 256, 0, st>>>(x, w, M, N, K, e);
+      else if (e.w_il)
+        gemm_frag_kernel<MODE, true, false><<<blocks, 256, 0, st>>>(x, w, M, N, K, e);
+      else if (e.x_il)
+        gemm_frag_kernel<MODE, false, true><<<blocks, 256, 0, st>>>(x, w, M, N, K, e);
       else
-        gemm_frag_kernel<MODE, false><<<blocks, 256, 0, st>>>((const bf16*)X, (const bf16*)W, M, N, K, e);
+        gemm_frag_kernel<MODE, false, false><<<blocks, 256, 0, st>>>(x, w, M, N, K, e);
       return;
     }
     const long big_tiles = (long)((M + LBM - 1) / LBM) * ((N + LBN - 1) / LBN);

@@ -39,10 +39,11 @@ void launch_lora(int dt, void* W, const void* A, const void* B, int N, int K, in
 //            otherwise row m sits at position m % seq_len (prompt pass)
 //   g == nullptr: no LayerNorm, x[m] = round(h[m]) (post-LN models)
 //   e_il:    layout of E (0 row-major, else the inference layout)
-//   x_mt:    0: x row-major [M, d]; > 0: x fragment-tiled with x_mt row tiles (xt_off)
+//   x_lay:   layout of x (act_off): 0 row-major [M, d]; > 0 fragment-tiled with x_lay
+//            row tiles (decode); < 0 the inference layout with il = -x_lay (prompt pass)
 void launch_embed_norm(int dt, const int32_t* ids, const int32_t* pos_dev, int seq_len,
                        const void* E, const void* P, const void* g, const void* b, float eps,
-                       float* h, void* x, int M, int d, int vocab, int e_il, int x_mt,
+                       float* h, void* x, int M, int d, int vocab, int e_il, int x_lay,
                        hipStream_t st);
 
 // Word-embedding gather only: xe[m] = E[ids[m]] (width de), storage type.
@@ -55,10 +56,10 @@ void launch_embed_gather(int dt, const int32_t* ids, const void* E, void* xe, in
 //      (parts are [nsplit][M][d]; r indexes them)
 //   post == 0: x[r] = round(LN(h[row]))             (pre-LN: h untouched by the norm)
 //   post == 1: h[row] = LN(h[row]); x[r] = round(h[row])  (post-LN)
-//   x_mt > 0: x is written fragment-tiled (xt_off) for a decode projection
+//   x_lay:   layout of x as for launch_embed_norm (act_off)
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias,
                  const void* g, const void* b, float eps, void* x, int M, int d,
-                 int row_stride, int row_offset, int post, int x_mt, hipStream_t st);
+                 int row_stride, int row_offset, int post, int x_lay, hipStream_t st);
 
 // ---- GEMM epilogues ------------------------------------------------------------
 enum Epi { EPI_QKV = 0, EPI_RESID, EPI_RELU, EPI_POSADD, EPI_F32 };
@@ -81,6 +82,10 @@ struct EpiArgs {
   float* out_f32 = nullptr;       // [M, N]
   // layout of the bf16 weight W: 0 row-major, else the inference layout (il_off)
   int w_il = 0;
+  // layout of the bf16 activations X (over K) and `out` (over N): 0 row-major, else the
+  // inference layout with that il (il_off), whose 16 x 32 fragments are whole cache lines
+  int x_il = 0;
+  int o_il = 0;
 };
 
 // Y[M,N] = X[M,K] W[N,K]^T with the epilogue (prompt-pass shapes, M large).
@@ -153,9 +158,10 @@ void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, int 
 
 // ---- attention ---------------------------------------------------------------------
 // Causal attention of the prompt pass: q [B*S, d] (scaled), keys/values of
-// positions 0..S-1 in the layer's cache; o [B*S, d] storage type.
+// positions 0..S-1 in the layer's cache; o [B*S, d] storage type, in the inference
+// layout with o_il (bf16; 0 row-major).
 void launch_attn_prefill(int dt, const void* q, const void* k_cache, const void* v_cache,
-                         void* o, int B, int S, int H, int D, int S_max, hipStream_t st);
+                         void* o, int B, int S, int H, int D, int S_max, int o_il, hipStream_t st);
 
 // One decode step.  qkv = sum of `splits` partials [splits][B][3d] + b_qkv: q is
 // scaled and rounded, k and v are rounded and appended at position *pos_dev;
