@@ -408,6 +408,182 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16* __re
   }
 }
 
+// Prompt pass, bf16, K and V of one (sequence, head) resident in LDS.  One WG of 8
+// waves per (sequence, head): the head's keys go to LDS row-major and its values
+// transposed (64 KB each at most), once; then every wave works through 16-query
+// blocks with no further block barrier, taking blocks w and 15 - w of each 16 so the
+// causal work is even.  Scores are formed transposed, S^T = K Q^T, so each lane holds
+// four consecutive keys of one query: exactly the B operand of the 16 x 16 x 16 MFMA,
+// which then computes O^T = V^T P^T straight from registers.  Online softmax per 32
+// keys (running max, per-lane partial sums merged at the end); P enters the product
+// as bf16 high and low parts (p = hi + lo to ~16 bits).  Both LDS arrays are
+// XOR-swizzled by 16-byte chunk so the 16 lanes that read 16 keys (or 16 value rows)
+// at one offset hit distinct banks.
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ short bf_bits(bf16 v) { return (short)v; }
+// v combined with the v of lane l ^ 16 (row swap) or l ^ 32 (half swap), gfx950: the
+// swap returns each lane's own value and its partner's, and max and + are commutative,
+// so both lanes of a pair get the same result.
+__device__ __forceinline__ float max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+constexpr int kPfKV = 32768;           // bf16 elements of each of K and V^T in LDS
+// Keys padded for the LDS layout (a multiple of 128, at least 128), or 0 when the head
+// does not fit.
+static int pf_pad(int S, int D) {
+  const int sp = S <= 128 ? 128 : (S + 127) / 128 * 128;
+  return sp * D <= kPfKV ? sp : 0;
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_prefill_lds_kernel(const bf16* __restrict__ q,
+                                                               const bf16* __restrict__ kc,
+                                                               const bf16* __restrict__ vc,
+                                                               bf16* __restrict__ o, int S, int S_pad,
+                                                               int H, int S_max, int o_il) {
+  constexpr int NCH = D / 8;             // 16-byte chunks per key row
+  constexpr int RPB = 128 / D;           // key rows per 256 bytes
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kPfKV];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[kPfKV];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x, b = bh / H, h = bh - b * H, d = H * D;
+  const size_t head = ((size_t)b * H + h) * S_max * D;
+  const int fr = lane & 15, fg = lane >> 4;
+
+  // K row `key`, chunk c at chunk c ^ ((key / RPB) mod NCH) of the row
+  for (int i = tid; i < S_pad * NCH; i += 512) {
+    const int key = i / NCH, c = i - key * NCH;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (key < S) v = *reinterpret_cast<const uint4*>(kc + head + (size_t)key * D + c * 8);
+    *reinterpret_cast<uint4*>(&Ks[key * D + ((c ^ ((key / RPB) & (NCH - 1))) << 3)]) = v;
+  }
+  // V^T row `dim` (S_pad keys), chunk j (keys 8 j .. + 8) at chunk j ^ (dim mod 16); each
+  // thread transposes an 8 keys x 8 dims block in registers
+  for (int i = tid; i < (S_pad / 8) * NCH; i += 512) {
+    const int kb = i / NCH, c = i - kb * NCH;
+    uint32_t e[8][4];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int key = kb * 8 + r;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (key < S) v = *reinterpret_cast<const uint4*>(vc + head + (size_t)key * D + c * 8);
+      e[r][0] = v.x; e[r][1] = v.y; e[r][2] = v.z; e[r][3] = v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sh = (j & 1) * 16, wd = j >> 1;
+      uint32_t w4[4];
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr)
+        w4[pr] = ((e[2 * pr][wd] >> sh) & 0xffffu) | (((e[2 * pr + 1][wd] >> sh) & 0xffffu) << 16);
+      const int dim = c * 8 + j;
+      *reinterpret_cast<uint4*>(&Vt[dim * S_pad + ((kb ^ (dim & 15)) << 3)]) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
+  __syncthreads();
+
+  const int nqb = (S + 15) / 16;
+  for (int base = 0; base < nqb; base += 16) {
+    for (int half = 0; half < 2; ++half) {
+      const int qb = base + (half ? 15 - wv : wv);
+      if (qb >= nqb) continue;
+      const int q0 = qb * 16, qi = q0 + fr;          // this lane's query (all 4 lane groups)
+      const int nkt = (min(q0 + 16, S) + 15) / 16;  // key tiles up to the block's last query
+      // Q^T as the B operand: lane holds query qi, dims 32 c + 8 fg .. + 8
+      bf16x8 qb8[D / 32];
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        qb8[c] = qi < S ? *reinterpret_cast<const bf16x8*>(q + ((size_t)b * S + qi) * d + h * D + c * 32 + fg * 8)
+                        : bf16x8{};
+      // O^T: oacc[t][r] = O(query qi, dim 16 t + 4 fg + r), unnormalised
+      f32x4 oacc[D / 16];
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float m = -INFINITY, lsum = 0.f;               // running max; this lane's share of the sum
+      for (int k0 = 0; k0 < nkt * 16; k0 += 32) {
+        // S^T for keys k0 .. k0 + 31: st[t2][r] = score(key k0 + 16 t2 + 4 fg + r, query qi)
+        f32x4 st[2];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          st[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const int key = k0 + t2 * 16 + fr;       // A-operand row of this lane
+          const int sw = (key / RPB) & (NCH - 1);
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[key * D + (((c * 4 + fg) ^ sw) << 3)]);
+            st[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb8[c], st[t2], 0, 0, 0);
+          }
+        }
+        float cm = -INFINITY;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + t2 * 16 + fg * 4 + r;
+            if (key > qi || key >= S) st[t2][r] = -INFINITY;
+            cm = fmaxf(cm, st[t2][r]);
+          }
+        cm = max32(max16(cm));
+        const float mn = fmaxf(m, cm);
+        const float sc = m == -INFINITY ? 0.f : __expf(m - mn);
+        m = mn;
+        lsum *= sc;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) oacc[t] *= sc;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          bf16x4 ph, pl;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = st[t2][r] == -INFINITY ? 0.f : __expf(st[t2][r] - mn);
+            lsum += p;
+            const bf16 hi = f2bf(p);
+            ph[r] = bf_bits(hi);
+            pl[r] = bf_bits(f2bf(p - bf2f(hi)));
+          }
+          // V^T fragment: dim 16 t + fr, keys k0 + 16 t2 + 4 fg .. + 4 (half a swizzled chunk)
+          const int chunk = ((k0 + t2 * 16) >> 3) + (fg >> 1);
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t) {
+            const int dim = t * 16 + fr;
+            const bf16x4 va = *reinterpret_cast<const bf16x4*>(&Vt[dim * S_pad + ((chunk ^ (dim & 15)) << 3) + ((fg & 1) << 2)]);
+            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, oacc[t], 0, 0, 0);
+            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, oacc[t], 0, 0, 0);
+          }
+        }
+      }
+      // the query's sum: the four lane groups' shares (the same value in every lane)
+      lsum = sum32(sum16(lsum));
+      if (qi < S) {
+        const float inv = 1.f / lsum;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          const int dim = t * 16 + fg * 4;
+          uint2 u;
+          u.x = (uint32_t)f2bf(oacc[t][0] * inv) | ((uint32_t)f2bf(oacc[t][1] * inv) << 16);
+          u.y = (uint32_t)f2bf(oacc[t][2] * inv) | ((uint32_t)f2bf(oacc[t][3] * inv) << 16);
+          *reinterpret_cast<uint2*>(o + il_off(b * S + qi, h * D + dim, d, o_il)) = u;
+        }
+      }
+    }
+  }
+}
+
 // fp32 models (tiny workload): one WG of 64 threads per (query, sequence, head).
 __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __restrict__ q,
                                                               const float* __restrict__ kc,
@@ -447,7 +623,18 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __res
 
 void launch_attn_prefill(int dt, const void* q, const void* k_cache, const void* v_cache, void* o,
                          int B, int S, int H, int D, int S_max, int o_il, hipStream_t st) {
-  if (dt == DT_BF16) {
+  if (dt == DT_BF16 && (D == 32 || D == 64 || D == 128) && pf_pad(S, D)) {
+    const int sp = pf_pad(S, D);
+    if (D == 128)
+      attn_prefill_lds_kernel<128><<<B * H, 512, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
+                                                          (const bf16*)v_cache, (bf16*)o, S, sp, H, S_max, o_il);
+    else if (D == 64)
+      attn_prefill_lds_kernel<64><<<B * H, 512, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
+                                                         (const bf16*)v_cache, (bf16*)o, S, sp, H, S_max, o_il);
+    else
+      attn_prefill_lds_kernel<32><<<B * H, 512, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
+                                                         (const bf16*)v_cache, (bf16*)o, S, sp, H, S_max, o_il);
+  } else if (dt == DT_BF16) {
     dim3 grid((S + 63) / 64, B * H);
     if (D == 64)
       attn_prefill_bf16_kernel<64><<<grid, 256, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
