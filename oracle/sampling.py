@@ -1,0 +1,130 @@
+"""Oracle for the sampling and log-probability extension of the generation step.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg; the product path never calls it.
+
+The experience the actor generates is "sampled" autoregressively (DeepSpeed-Chat
+paper summary, section on the RLHF pipeline: the actor produces answers to the
+queries), and the PPO step that follows needs the log-probability of every generated
+token under the actor.  The pages give no sampler.  Reading taken here:
+
+* temperature T > 0: the next token is drawn from softmax(logits / T) by the
+  Gumbel-max rule, token = argmax_n (logit_n / T + G_n) with G_n = -log(-log U_n),
+  which yields exactly that distribution for i.i.d. uniform U_n;  T = 0 is greedy
+  (lowest index on ties);
+* U_n comes from the counter-based generator Philox4x64-10 (Salmon, Moraes, Dror,
+  Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), counter
+  (n, row, position of the generated token, 0), key (seed, 0); U = (top 24 bits of
+  the first output word + 1/2) / 2^24, single precision as in the kernel;
+* the log-probability reported for a token t is logit_t / T' - logsumexp(logits / T')
+  with T' = T (T' = 1 for greedy), computed here in float64.
+"""
+from __future__ import annotations
+
+from typing import List, Tuple
+
+import numpy as np
+
+from oracle import opt_he as O
+
+M32 = np.uint64(0xFFFFFFFF)
+# Philox4x64 round multipliers and Weyl key increments (Salmon et al., 2011)
+PHILOX_M0 = np.uint64(0xD2E7470EE14C6C93)
+PHILOX_M1 = np.uint64(0xCA5A826395121157)
+PHILOX_W0 = np.uint64(0x9E3779B97F4A7C15)
+PHILOX_W1 = np.uint64(0xBB67AE8584CAA73B)
+
+
+def _mulhilo64(a: np.uint64, b: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(high, low) 64-bit halves of the 128-bit product a * b, elementwise."""
+    b = np.asarray(b, dtype=np.uint64)
+    a0, a1 = a & M32, a >> np.uint64(32)
+    b0, b1 = b & M32, b >> np.uint64(32)
+    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1     # each < 2^64
+    mid = (p00 >> np.uint64(32)) + (p01 & M32) + (p10 & M32)
+    hi = p11 + (p01 >> np.uint64(32)) + (p10 >> np.uint64(32)) + (mid >> np.uint64(32))
+    lo = a * b                                                   # wraps mod 2^64
+    return hi, lo
+
+
+def philox4x64_10(counter, key) -> np.ndarray:
+    """Ten rounds of Philox4x64 on counters [4, ...] with key (k0, k1); returns [4, ...]."""
+    with np.errstate(over="ignore"):
+        c0, c1, c2, c3 = (np.asarray(x, dtype=np.uint64) for x in counter)
+        k0, k1 = np.uint64(key[0]), np.uint64(key[1])
+        for _ in range(10):
+            hi0, lo0 = _mulhilo64(PHILOX_M0, c0)
+            hi1, lo1 = _mulhilo64(PHILOX_M1, c2)
+            c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+            k0, k1 = k0 + PHILOX_W0, k1 + PHILOX_W1
+    return np.stack([c0, c1, c2, c3])
+
+
+def uniforms(seed: int, rows: np.ndarray, position: int, V: int) -> np.ndarray:
+    """U[b, n] in (0, 1), float32, for batch rows `rows` generating at `position`."""
+    rows = np.asarray(rows, dtype=np.uint64)
+    n = np.arange(V, dtype=np.uint64)
+    ctr = (np.broadcast_to(n[None, :], (len(rows), V)),
+           np.broadcast_to(rows[:, None], (len(rows), V)),
+           np.full((len(rows), V), position, dtype=np.uint64),
+           np.zeros((len(rows), V), dtype=np.uint64))
+    w = philox4x64_10(ctr, (np.uint64(seed), np.uint64(0)))[0]
+    top = (w >> np.uint64(40)).astype(np.float32)
+    return (top + np.float32(0.5)) * np.float32(2.0 ** -24)
+
+
+def gumbel(u: np.ndarray) -> np.ndarray:
+    """G = -log(-log U) in float32."""
+    u = np.asarray(u, dtype=np.float32)
+    return -np.log(-np.log(u))
+
+
+def logsumexp(x: np.ndarray, axis: int = -1) -> np.ndarray:
+    """log(sum(exp(x))) along axis, float64, shifted by the maximum."""
+    x = np.asarray(x, dtype=np.float64)
+    m = np.max(x, axis=axis, keepdims=True)
+    return (m + np.log(np.sum(np.exp(x - m), axis=axis, keepdims=True))).squeeze(axis)
+
+
+def pick(logits: np.ndarray, temperature: float, seed: int, rows: np.ndarray,
+         position: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One step for rows of logits [B, V] (float64).
+
+    Returns (tokens [B], log-probabilities [B], decision margin [B]): the margin is the
+    gap between the best and second-best of the quantity maximised (logits for greedy,
+    logit / T + G for sampling), the part of the decision a rounding change can flip.
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    if temperature > 0:
+        scaled = logits / temperature
+        y = scaled + gumbel(uniforms(seed, rows, position, logits.shape[1])).astype(np.float64)
+    else:
+        scaled = logits
+        y = logits
+    tok = O.argmax_lowest(y)
+    top2 = np.sort(y, axis=1)[:, -2:]
+    lp = scaled[np.arange(len(tok)), tok] - logsumexp(scaled, axis=1)
+    return tok, lp, top2[:, 1] - top2[:, 0]
+
+
+def sampled_generate(model: O.OracleModel, prompts, gen_len: int, max_seq: int, temperature: float,
+                     seed: int, forced=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray, List[np.ndarray]]:
+    """Generate gen_len tokens per row (the greedy loop of opt_he.greedy_generate with
+    `pick` as the rule).  Token j of every row is generated at position S + j.
+    Returns (tokens [B, gen_len], log-probabilities [B, gen_len], margins [B, gen_len],
+    logits per step)."""
+    prompts = np.asarray(prompts)
+    B, S = prompts.shape
+    rows = np.arange(B)
+    toks = np.zeros((B, gen_len), dtype=np.int64)
+    lps = np.zeros((B, gen_len))
+    margins = np.zeros((B, gen_len))
+    lg, cache = model.prefill(prompts, max_seq)
+    logits = [lg]
+    toks[:, 0], lps[:, 0], margins[:, 0] = pick(lg, temperature, seed, rows, S)
+    for j in range(1, gen_len):
+        fed = toks[:, j - 1] if forced is None else np.asarray(forced)[:, j - 1]
+        lg = model.decode(fed, cache)
+        logits.append(lg)
+        toks[:, j], lps[:, j], margins[:, j] = pick(lg, temperature, seed, rows, S + j)
+    return toks, lps, margins, logits
