@@ -13,9 +13,10 @@ token under the actor.  The pages give no sampler.  Reading taken here:
   which yields exactly that distribution for i.i.d. uniform U_n;  T = 0 is greedy
   (lowest index on ties);
 * U_n comes from the counter-based generator Philox4x64-10 (Salmon, Moraes, Dror,
-  Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), counter
-  (n, row, position of the generated token, 0), key (seed, 0); U = (top 24 bits of
-  the first output word + 1/2) / 2^24, single precision as in the kernel;
+  Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011): one block per four
+  columns, counter (n div 4, row, position of the generated token, 0), key (seed, 0),
+  output word n mod 4; U = (top 24 bits of that word + 1/2) / 2^24, single precision
+  as in the kernel;
 * the log-probability reported for a token t is logit_t / T' - logsumexp(logits / T')
   with T' = T (T' = 1 for greedy), computed here in float64.
 """
@@ -63,12 +64,14 @@ def philox4x64_10(counter, key) -> np.ndarray:
 def uniforms(seed: int, rows: np.ndarray, position: int, V: int) -> np.ndarray:
     """U[b, n] in (0, 1), float32, for batch rows `rows` generating at `position`."""
     rows = np.asarray(rows, dtype=np.uint64)
-    n = np.arange(V, dtype=np.uint64)
-    ctr = (np.broadcast_to(n[None, :], (len(rows), V)),
-           np.broadcast_to(rows[:, None], (len(rows), V)),
-           np.full((len(rows), V), position, dtype=np.uint64),
-           np.zeros((len(rows), V), dtype=np.uint64))
-    w = philox4x64_10(ctr, (np.uint64(seed), np.uint64(0)))[0]
+    nb = (V + 3) // 4
+    n4 = np.arange(nb, dtype=np.uint64)
+    ctr = (np.broadcast_to(n4[None, :], (len(rows), nb)),
+           np.broadcast_to(rows[:, None], (len(rows), nb)),
+           np.full((len(rows), nb), position, dtype=np.uint64),
+           np.zeros((len(rows), nb), dtype=np.uint64))
+    w = philox4x64_10(ctr, (np.uint64(seed), np.uint64(0)))       # [4, rows, nb]
+    w = np.moveaxis(w, 0, -1).reshape(len(rows), 4 * nb)[:, :V]    # column n = word n % 4 of block n // 4
     top = (w >> np.uint64(40)).astype(np.float32)
     return (top + np.float32(0.5)) * np.float32(2.0 ** -24)
 
