@@ -414,6 +414,35 @@ def main():
                            "launches": s.launches}
         log(f"roofline: {json.dumps(res['roofline'])}")
 
+        # sampled generation (temperature 0.7, Gumbel-max with Philox4x64-10) with per-token
+        # log-probabilities, same shape and fused weights: whole-generation time beside the
+        # greedy one, and the LM head's time per launch in each mode
+        with torch.cuda.stream(st):
+            lpb = torch.empty(B, G, dtype=torch.float32, device="cuda")
+            smp = he.he_sampling(0.7, 1234)
+            E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            he.he_fuse_lora(ctx, lt)
+            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp, out.data_ptr(), lpb.data_ptr())  # graph capture
+            E[0].record(st)
+            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp, out.data_ptr(), lpb.data_ptr())
+            E[1].record(st)
+            he.he_kernel_timer(ctx, he.HE_K_LMHEAD, True)
+            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, 8, smp, out.data_ptr(), lpb.data_ptr())
+            lm_s = he.he_kernel_stats(ctx, he.HE_K_LMHEAD)
+            he.he_kernel_timer(ctx, he.HE_K_LMHEAD, False)
+            he.he_unfuse_lora(ctx, lt)
+            he.he_sync(ctx)
+            torch.cuda.synchronize()
+        t_smp = E[0].elapsed_time(E[1]) / 1e3
+        lps = lpb.cpu().numpy()
+        res["sampled"] = {
+            "temperature": 0.7, "gen_ms": t_smp * 1e3, "gen_tokens_per_s": B * G / t_smp,
+            "vs_greedy_gen": (t_pre + t_dec) / t_smp,
+            "lmhead_us_sampled_logprobs": lm_s.total_ms / lm_s.launches * 1e3 if lm_s.launches else None,
+            "lmhead_us_greedy": kern["lmhead"]["avg_us"] if "lmhead" in kern else None,
+            "mean_logprob": float(lps.mean()), "logprobs_finite": bool((lps == lps).all())}
+        log(f"sampled: {json.dumps(res['sampled'])}")
+
     with torch.cuda.stream(st):
         he.he_release_cache(ctx)
         he.he_sync(ctx)

@@ -239,6 +239,32 @@ he_status he_decode_step(he_ctx* ctx, const int32_t* d_in, int32_t* d_next, floa
 he_status he_generate(he_ctx* ctx, const int32_t* d_prompt, int32_t B, int32_t S_p,
                       int32_t S_g, int32_t* d_out);
 
+/* Pick rule of he_generate_ex.  The paper summary's pipeline section has the actor
+ * generate (sample) answers, and the PPO step that follows scores each generated
+ * token by its log-probability under the actor; the pages give no sampler.
+ * temperature == 0: greedy (largest logit, lowest index on ties).
+ * temperature  > 0: the next token is drawn from softmax(logits / temperature) by
+ *   the Gumbel-max rule: argmax_n (logit_n / temperature + G_n), G_n = -log(-log U_n),
+ *   U_n = (top 24 bits of word n mod 4 of Philox4x64-10 (Salmon et al., SC 2011)
+ *   at counter (n div 4, batch row, position of the token, 0), key (seed, 0) + 1/2)
+ *   / 2^24.  A pick is a function of (seed, row, position, logits) only: the same
+ *   seed reproduces a generation exactly. */
+typedef struct he_sampling {
+  float temperature;
+  uint64_t seed;
+} he_sampling;
+
+/* he_generate with a pick rule and per-token log-probabilities.  smp == NULL is
+ * greedy.  d_out [B, S_g] int32 as he_generate; when d_logprobs != NULL it
+ * receives [B, S_g] float32: for each generated token t, log softmax(logits / T')_t
+ * with T' = temperature (1 for greedy), the row's logsumexp combined over vocabulary
+ * blocks in a fixed order.  Device memory, caller-owned; written by the end of the
+ * call's stream work.
+ * Errors as he_generate, plus HE_E_ARG for a temperature that is negative, not
+ * finite, or so small that its reciprocal overflows. */
+he_status he_generate_ex(he_ctx* ctx, const int32_t* d_prompt, int32_t B, int32_t S_p,
+                         int32_t S_g, const he_sampling* smp, int32_t* d_out, float* d_logprobs);
+
 /* Reward scoring (page 1, pipeline section: the reward model gives each response
  * a scalar score): full causal pass over d_ids [B, S] of a HE_HEAD_SCALAR model,
  * d_reward [B] float32 = (h[S-1] proj_out^T) . score_w.  Uses the workspace.

@@ -29,7 +29,8 @@ def _declared():
 
 def test_exports_every_declared_call():
     names = _declared()
-    assert "he_generate" in names and "he_fuse_lora" in names and len(names) >= 17
+    assert "he_generate" in names and "he_generate_ex" in names and "he_fuse_lora" in names
+    assert len(names) >= 18
     L = ctypes.CDLL(he.LIB_PATH)
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
@@ -144,6 +145,13 @@ def test_argument_checks():
     assert _status(he.he_prefill, ctx, 0, 2, 16, P) == he.HE_E_ARG    # NULL ids
     assert _status(he.he_score, ctx, P, 2, 16, P) == he.HE_E_UNSUPPORTED
     assert _status(he.he_generate, ctx, P, 2, 16, 0, P) == he.HE_E_ARG
+    # sampled generation: temperature must be finite and >= 0; NULL rule = greedy
+    for t in (-0.5, float("nan"), float("inf"), 1e-45):
+        assert _status(he.he_generate_ex, ctx, P, 2, 16, 8, he.he_sampling(t, 1), P, P) == he.HE_E_ARG
+    he.he_generate_ex(ctx, P, 2, 16, 8, None, P, P)
+    he.he_generate_ex(ctx, P, 2, 16, 8, he.he_sampling(0.7, 123), P, 0)
+    assert _status(he.he_generate_ex, ctx, P, 2, 16, 18, he.he_sampling(1.0, 1), P, P) == he.HE_E_RANGE
+    assert _status(he.he_generate_ex, ctx, 0, 2, 16, 8, he.he_sampling(1.0, 1), P, P) == he.HE_E_ARG
     bad = he.he_lora_table(rank=0, alpha=1.0, pairs=(he.he_lora_pair * 12)())
     assert _status(he.he_fuse_lora, ctx, bad) == he.HE_E_ARG
     assert "rank" in he.he_last_error(ctx)

@@ -112,6 +112,36 @@ __device__ __forceinline__ size_t act_off(int m, int k, int K, int lay) {
   return lay > 0 ? xt_off(m, k, lay) : il_off(m, k, K, -lay);
 }
 
+// Counter-based generator Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): ten rounds of the 4 x 64-bit bijection on the
+// counter, the key advanced by the Weyl increments after every round.
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+    k0 += W0; k1 += W1;
+  }
+}
+
+// Gumbel noise G = -log(-log U) of vocabulary columns 4 n4 .. 4 n4 + 3 for batch row
+// `row` generating the token at `position`: one generator block at counter
+// (n4, row, position, 0), key (seed, 0); column 4 n4 + w takes word w, and
+// U = (its top 24 bits + 1/2) / 2^24.
+__device__ __forceinline__ void gumbel4(uint64_t seed, int row, int position, int n4, float g[4]) {
+  uint64_t c[4] = {(uint64_t)n4, (uint64_t)row, (uint64_t)position, 0ull};
+  philox4x64_10(c, seed, 0ull);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float u = ((float)(uint32_t)(c[w] >> 40) + 0.5f) * 0x1p-24f;
+    g[w] = -logf(-logf(u));
+  }
+}
+
 // Sum over the block in a fixed order (deterministic).  `red` holds >= nwaves floats.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;

@@ -79,8 +79,18 @@ struct he_ctx {
   int32_t* best_idx = nullptr;
   int32_t* ids_cur = nullptr;
   int32_t* tokens = nullptr;
-  int32_t* pos_dev = nullptr;
+  int32_t* pos_dev = nullptr;     // position of the token the next step feeds
+  int32_t* pos_next = nullptr;    // position of the token being picked (LM head -> finalize)
+  float* logp = nullptr;          // [B_max][S_max + 1] log-probabilities of the picks
+  float* best_lg = nullptr;       // per (row, LM-head column block): pick's tempered logit,
+  float* blk_max = nullptr;       // the block's largest tempered logit and its sum of
+  float* blk_sum = nullptr;       // exponentials
   int n_argmax_blocks = 0, argmax_cap = 0;
+  // pick rule of the LM head: temperature 0 greedy, else Gumbel-max sampling; and
+  // whether log-probabilities are formed
+  float inv_temp = 0.f;
+  uint64_t seed = 0;
+  bool want_logp = false;
   // decode GEMM plans and activation row tiles for the current batch (set by the
   // prompt pass)
   GemvPlan p_qkv, p_out, p_fc1, p_fc2, p_lm;
@@ -95,6 +105,9 @@ struct he_ctx {
   hipGraphExec_t graph[2] = {nullptr, nullptr};
   int graph_B = -1;
   bool graph_fused = false;
+  float graph_itemp = 0.f;        // pick rule the graphs were captured with
+  uint64_t graph_seed = 0;
+  bool graph_logp = false;
   bool capturing = false;
 
   Timer timers[HE_K_COUNT];
@@ -252,16 +265,21 @@ static void decode_partials(he_ctx* c, const void* X, const void* W, int B, int 
   launch_gemv(c->dt, X, W, B, N, K, p, g, st);
 }
 
-// Tied LM head over z (x rows 0..B-1) + greedy pick; advances the position counter.
+// Tied LM head over z (x rows 0..B-1) + the pick (greedy or sampled, with its
+// log-probability when asked); advances the position counter.
 static void enqueue_lm_head(he_ctx* c, int B, bool want_logits) {
   const int d = c->d, dt = c->dt;
   const size_t es = esize(dt);
   hipStream_t st = c->stream;
-  if (dt == DT_BF16 && c->p_lm.splits > 1) {
+  SampleArgs smp;
+  smp.inv_temp = c->inv_temp;
+  smp.seed = c->seed;
+  if (c->want_logp) { smp.best_lg = c->best_lg; smp.blk_max = c->blk_max; smp.blk_sum = c->blk_sum; }
+  if (c->p_lm.splits > 1) {
     run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d, [&] {
       decode_partials(c, c->x, c->wt.tok_emb, B, c->V, d, c->p_lm, e_il(c), st);
       launch_reduce_argmax(c->parts, c->p_lm.splits, B, c->V, want_logits ? c->logits : nullptr,
-                           c->best_val, c->best_idx, c->n_argmax_blocks, c->pos_dev, st);
+                           c->best_val, c->best_idx, c->n_argmax_blocks, c->pos_dev, c->pos_next, smp, st);
     });
   } else {
     GemvArgs g;
@@ -271,12 +289,14 @@ static void enqueue_lm_head(he_ctx* c, int B, bool want_logits) {
     g.best_val = c->best_val;
     g.best_idx = c->best_idx;
     g.n_blocks = c->n_argmax_blocks;
-    g.bump = c->pos_dev;
+    g.pos_dev = c->pos_dev;
+    g.pos_next = c->pos_next;
+    g.smp = smp;
     run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d,
           [&] { launch_gemv(dt, c->x, c->wt.tok_emb, B, c->V, d, c->p_lm, g, st); });
   }
-  launch_argmax_finalize(c->best_val, c->best_idx, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
-                         c->max_seq + 1, c->pos_dev, nullptr, st);
+  launch_argmax_finalize(c->best_val, c->best_idx, smp, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
+                         c->want_logp ? c->logp : nullptr, c->max_seq + 1, c->pos_next, c->pos_dev, nullptr, st);
 }
 
 // Prompt pass of a pre-LN LM-head model; leaves z (final LN of the last rows) in x.
@@ -688,7 +708,12 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   const size_t o_bi = take((size_t)bpad * argmax_cap * 4);
   const size_t o_ids = take((size_t)bpad * 4);
   const size_t o_tok = take((size_t)max_batch * (max_seq + 1) * 4);
+  const size_t o_logp = take((size_t)max_batch * (max_seq + 1) * 4);
+  const size_t o_blg = take((size_t)bpad * argmax_cap * 4);
+  const size_t o_bmx = take((size_t)bpad * argmax_cap * 4);
+  const size_t o_bsm = take((size_t)bpad * argmax_cap * 4);
   const size_t o_pos = take(256);
+  const size_t o_posn = take(256);
   c->max_batch = max_batch;
   c->max_seq = max_seq;
   c->bpad = bpad;
@@ -728,6 +753,11 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   c->ids_cur = (int32_t*)(scratch + o_ids);
   c->tokens = (int32_t*)(scratch + o_tok);
   c->pos_dev = (int32_t*)(scratch + o_pos);
+  c->pos_next = (int32_t*)(scratch + o_posn);
+  c->logp = (float*)(scratch + o_logp);
+  c->best_lg = (float*)(scratch + o_blg);
+  c->blk_max = (float*)(scratch + o_bmx);
+  c->blk_sum = (float*)(scratch + o_bsm);
   c->cache = true;
   c->prefilled = false;
   // The decode GEMM reads X rows up to the next multiple of 16: give the padding
@@ -768,10 +798,19 @@ static he_status do_prefill(he_ctx* c, const int32_t* ids, int B, int S, bool wa
   return HE_OK;
 }
 
+// Greedy picks without log-probabilities: the rule of he_prefill, he_decode_step and
+// he_generate.
+static void set_greedy(he_ctx* c) {
+  c->inv_temp = 0.f;
+  c->seed = 0;
+  c->want_logp = false;
+}
+
 he_status he_prefill(he_ctx* c, const int32_t* ids, int32_t B, int32_t S, int32_t* d_next, float* d_logits) {
   if (!c) return HE_E_ARG;
   he_status s = prefill_checks(c, ids, B, S, d_next);
   if (s != HE_OK) return s;
+  set_greedy(c);
   if (c->validate_only) {
     c->prefilled = true; c->cur_B = B; c->cur_pos = S;
     return HE_OK;
@@ -795,7 +834,9 @@ static he_status run_step(he_ctx* c, bool want_logits) {
   const bool graph = c->use_graph && !any_timer_armed(c);
   if (graph) {
     hipGraphExec_t& ge = c->graph[want_logits ? 1 : 0];
-    if (c->graph_B != B || c->graph_fused != c->fused) drop_graphs(c);
+    if (c->graph_B != B || c->graph_fused != c->fused || c->graph_itemp != c->inv_temp ||
+        c->graph_seed != c->seed || c->graph_logp != c->want_logp)
+      drop_graphs(c);
     if (!ge) {
       hipGraph_t g = nullptr;
       HIP_TRY(c, hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal));
@@ -809,6 +850,9 @@ static he_status run_step(he_ctx* c, bool want_logits) {
       if (e != hipSuccess) { ge = nullptr; return hip_fail(c, e, "hipGraphInstantiate"); }
       c->graph_B = B;
       c->graph_fused = c->fused;
+      c->graph_itemp = c->inv_temp;
+      c->graph_seed = c->seed;
+      c->graph_logp = c->want_logp;
     }
     HIP_TRY(c, hipGraphLaunch(ge, c->stream));
   } else {
@@ -834,6 +878,7 @@ he_status he_decode_step(he_ctx* c, const int32_t* d_in, int32_t* d_next, float*
   he_status s = step_checks(c);
   if (s != HE_OK) return s;
   if (!d_in || !d_next) return set_err(c, HE_E_ARG, "NULL buffer");
+  set_greedy(c);
   if (c->validate_only) {
     if (c->fail_next_step) { c->fail_next_step = false; c->failed = true; return set_err(c, HE_E_HIP, "injected device fault"); }
     c->cur_pos += 1;
@@ -848,8 +893,8 @@ he_status he_decode_step(he_ctx* c, const int32_t* d_in, int32_t* d_next, float*
   return HE_OK;
 }
 
-he_status he_generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g, int32_t* d_out) {
-  if (!c) return HE_E_ARG;
+static he_status generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g,
+                          int32_t* d_out, float* d_logp) {
   he_status s = prefill_checks(c, d_prompt, B, S, d_out);
   if (s != HE_OK) return s;
   if (S_g < 1) return set_err(c, HE_E_ARG, "S_g %d < 1", S_g);
@@ -871,7 +916,30 @@ he_status he_generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, 
   }
   HIP_TRY(c, hipMemcpy2DAsync(d_out, (size_t)S_g * 4, c->tokens + S, (size_t)(c->max_seq + 1) * 4,
                               (size_t)S_g * 4, B, hipMemcpyDeviceToDevice, c->stream));
+  if (d_logp)
+    HIP_TRY(c, hipMemcpy2DAsync(d_logp, (size_t)S_g * 4, c->logp + S, (size_t)(c->max_seq + 1) * 4,
+                                (size_t)S_g * 4, B, hipMemcpyDeviceToDevice, c->stream));
   return HE_OK;
+}
+
+he_status he_generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g, int32_t* d_out) {
+  if (!c) return HE_E_ARG;
+  set_greedy(c);
+  return generate(c, d_prompt, B, S, S_g, d_out, nullptr);
+}
+
+he_status he_generate_ex(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g,
+                         const he_sampling* smp, int32_t* d_out, float* d_logprobs) {
+  if (!c) return HE_E_ARG;
+  const float t = smp ? smp->temperature : 0.f;
+  if (!(t >= 0.f) || !std::isfinite(t))
+    return set_err(c, HE_E_ARG, "temperature %g is not a finite value >= 0", (double)t);
+  const float it = t > 0.f ? 1.f / t : 0.f;
+  if (t > 0.f && !std::isfinite(it)) return set_err(c, HE_E_ARG, "temperature %g too small", (double)t);
+  c->inv_temp = it;
+  c->seed = smp && t > 0.f ? smp->seed : 0;
+  c->want_logp = d_logprobs != nullptr;
+  return generate(c, d_prompt, B, S, S_g, d_out, d_logprobs);
 }
 
 he_status he_score(he_ctx* c, const int32_t* d_ids, int32_t B, int32_t S, float* d_reward) {

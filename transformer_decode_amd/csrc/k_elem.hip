@@ -401,44 +401,63 @@ void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* b
 }
 
 // ---------------------------------------------------------------------------------
-// Greedy pick: reduce the per-block (max, index) pairs of a row; the lowest index
-// wins ties.  One wave per row.
+// Pick: reduce the per-block (pick value, index) pairs of a row, greedy or sampled;
+// the lowest index wins ties; optionally the log-probability.  One wave per row.
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
 __global__ __launch_bounds__(64) void argmax_finalize_kernel(
-    const float* __restrict__ best_val, const int32_t* __restrict__ best_idx, int nb,
-    int32_t* __restrict__ ids_cur, int32_t* __restrict__ tokens, int tok_stride,
-    const int32_t* __restrict__ pos_dev, int32_t* __restrict__ d_next) {
+    const float* __restrict__ best_val, const int32_t* __restrict__ best_idx, SampleArgs smp, int nb,
+    int32_t* __restrict__ ids_cur, int32_t* __restrict__ tokens, float* __restrict__ logp, int tok_stride,
+    const int32_t* __restrict__ pos_next, int32_t* __restrict__ pos_dev, int32_t* __restrict__ d_next) {
   const int m = blockIdx.x, l = threadIdx.x;
-  float bv = -INFINITY;
+  const bool lse = logp && smp.blk_max;
+  float bv = -INFINITY, bl = -INFINITY, mx = -INFINITY;
   int bi = 0x7fffffff;
   for (int i = l; i < nb; i += 64) {
-    float v = best_val[(size_t)m * nb + i];
-    int ix = best_idx[(size_t)m * nb + i];
-    if (better(v, ix, bv, bi)) { bv = v; bi = ix; }
+    const size_t o = (size_t)m * nb + i;
+    const float v = best_val[o];
+    const int ix = best_idx[o];
+    if (better(v, ix, bv, bi)) { bv = v; bi = ix; if (lse) bl = smp.best_lg[o]; }
+    if (lse) mx = fmaxf(mx, smp.blk_max[o]);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(bv, o, 64);
-    int oi = __shfl_xor(bi, o, 64);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    const float ov = __shfl_xor(bv, o, 64), ol = __shfl_xor(bl, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; bl = ol; }
+    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  }
+  float sum = 0.f;
+  if (lse) {
+    // sum over blocks of blk_sum * exp(blk_max - mx): each lane its blocks in order,
+    // then a fixed butterfly; lane 0's value is used
+    for (int i = l; i < nb; i += 64) {
+      const size_t o = (size_t)m * nb + i;
+      sum += smp.blk_sum[o] * expf(smp.blk_max[o] - mx);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
   }
   if (l == 0) {
+    const int p = *pos_next;
     if (bi == 0x7fffffff) bi = 0;
     if (ids_cur) ids_cur[m] = bi;
-    if (tokens) tokens[(size_t)m * tok_stride + *pos_dev] = bi;
+    if (tokens) tokens[(size_t)m * tok_stride + p] = bi;
+    if (lse) logp[(size_t)m * tok_stride + p] = bl - (mx + logf(sum));
     if (d_next) d_next[m] = bi;
+    if (m == 0 && pos_dev) *pos_dev = p;
   }
 }
 
-void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, int n_blocks, int M,
-                            int32_t* ids_cur, int32_t* tokens, int tok_stride,
-                            const int32_t* pos_dev, int32_t* d_next, hipStream_t st) {
-  argmax_finalize_kernel<<<M, 64, 0, st>>>(best_val, best_idx, n_blocks, ids_cur, tokens,
-                                           tok_stride, pos_dev, d_next);
+void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, const SampleArgs& smp,
+                            int n_blocks, int M, int32_t* ids_cur, int32_t* tokens, float* logp,
+                            int tok_stride, const int32_t* pos_next, int32_t* pos_dev, int32_t* d_next,
+                            hipStream_t st) {
+  argmax_finalize_kernel<<<M, 64, 0, st>>>(best_val, best_idx, smp, n_blocks, ids_cur, tokens, logp,
+                                           tok_stride, pos_next, pos_dev, d_next);
 }
 
 // ---------------------------------------------------------------------------------

@@ -137,7 +137,12 @@ struct IlArgs {
   float* best_val;                // ARGMAX: [M][n_blocks]
   int32_t* best_idx;
   int n_blocks;
-  int32_t* bump;
+  int32_t* pos_next;              // ARGMAX: gets *pos_dev + 1, the picked token's position
+  float inv_temp;                 // ARGMAX: pick rule (SampleArgs)
+  uint64_t seed;
+  float* best_lg;
+  float* blk_max;
+  float* blk_sum;
   bf16* q_out;                    // QKV
   bf16* k_cache;
   bf16* v_cache;
@@ -258,28 +263,48 @@ __global__ __launch_bounds__(NWK * 64) void gemv_il_kernel(const bf16* __restric
       }
   }
   if (OUT == GV_ARGMAX) {
-    // per batch row: max over this WG's FR * 16 rows of W, lowest index on ties
+    // per batch row over this WG's FR * 16 rows of W: the pick (largest logit, or
+    // tempered logit + Gumbel noise; lowest index on ties), its tempered logit, and the
+    // block's largest tempered logit and sum of exponentials, each in a fixed order
     __syncthreads();
+    const bool samp = a.inv_temp > 0.f;
+    const float sc = samp ? a.inv_temp : 1.f;
+    const int gpos = a.pos_dev ? *a.pos_dev + 1 : 0;
     for (int m = threadIdx.x; m < MT * 16; m += NWK * 64) {
       const int t = m >> 4, c = m & 15;
-      float bv = -INFINITY;
+      float bv = -INFINITY, blg = -INFINITY, mx = -INFINITY;
       int bi = min(rb0 * 16, a.N - 1);
       for (int f = 0; f < FR && rb0 + f < nrb; ++f)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4 v = red[0][f * MT + t][g * 16 + c];
+          const int n0 = (rb0 + f) * 16 + g * 4;
+          float gn[4] = {0.f, 0.f, 0.f, 0.f};
+          if (samp) gumbel4(a.seed, m, gpos, n0 >> 2, gn);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int n = (rb0 + f) * 16 + g * 4 + r;
-            if (v[r] > bv) { bv = v[r]; bi = n; }     // n increases: the first maximum stays
+            const float lg = v[r] * sc, y = lg + gn[r];
+            if (y > bv) { bv = y; bi = n0 + r; blg = lg; }   // n increases: the first maximum stays
+            mx = fmaxf(mx, lg);
           }
         }
+      float sum = 0.f;
+      if (a.blk_max)
+        for (int f = 0; f < FR && rb0 + f < nrb; ++f)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = red[0][f * MT + t][g * 16 + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sum += expf(v[r] * sc - mx);
+          }
       if (m < a.M) {
-        a.best_val[(size_t)m * a.n_blocks + blockIdx.x] = bv;
-        a.best_idx[(size_t)m * a.n_blocks + blockIdx.x] = bi;
+        const size_t o = (size_t)m * a.n_blocks + blockIdx.x;
+        a.best_val[o] = bv;
+        a.best_idx[o] = bi;
+        if (a.blk_max) { a.best_lg[o] = blg; a.blk_max[o] = mx; a.blk_sum[o] = sum; }
       }
     }
-    if (a.bump && blockIdx.x == 0 && threadIdx.x == 0) *a.bump += 1;
+    if (a.pos_next && blockIdx.x == 0 && threadIdx.x == 0) *a.pos_next = gpos;
   }
 }
 
@@ -350,40 +375,72 @@ __global__ __launch_bounds__(256) void reduce_relu_kernel(const float* __restric
   *reinterpret_cast<uint2*>(out + (mt ? xt_off(m, n, mt) : i4)) = u;
 }
 
-// logits[m][n] = sum_s parts[s][m][n]; per (m, block of 128 columns): max and its
-// lowest index -> best_val / best_idx.
+// One 128-column block of row m under the pick rule of SampleArgs: the thread holds
+// column n's logit v (ok: n < N).  Writes the block's pick value and index (lowest
+// index on ties) and, with blk_max, the pick's tempered logit, the largest tempered
+// logit and the sum of exp(tempered logit - that maximum); the two waves are merged in
+// a fixed order through `sh` (8 floats, 2 ints).
+__device__ __forceinline__ void pick_block128(bool ok, float v, int n, int m, int nb, float inv_temp,
+                                              uint64_t seed, int gpos, float* best_val, int32_t* best_idx,
+                                              float* best_lg, float* blk_max, float* blk_sum,
+                                              float* sh, int* shi) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const bool samp = inv_temp > 0.f;
+  const float lg = ok ? v * (samp ? inv_temp : 1.f) : -INFINITY;
+  float y = lg, blg = lg;
+  if (ok && samp) {
+    float g4[4];
+    gumbel4(seed, m, gpos, n >> 2, g4);
+    y = lg + g4[n & 3];
+  }
+  int idx = n;
+  float mx = lg;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float ov = __shfl_xor(y, o, 64), ol = __shfl_xor(blg, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    if (gv_better(ov, oi, y, idx)) { y = ov; idx = oi; blg = ol; }
+    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  }
+  if (lane == 0) { sh[wv] = y; shi[wv] = idx; sh[2 + wv] = blg; sh[4 + wv] = mx; }
+  __syncthreads();
+  const float bmx = fmaxf(sh[4], sh[5]);
+  float e = ok ? expf(lg - bmx) : 0.f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) e += __shfl_xor(e, o, 64);
+  if (lane == 0) sh[6 + wv] = e;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float by = sh[0], bl = sh[2];
+    int bi = shi[0];
+    if (gv_better(sh[1], shi[1], by, bi)) { by = sh[1]; bi = shi[1]; bl = sh[3]; }
+    const size_t o = (size_t)m * nb + blockIdx.x;
+    best_val[o] = by;
+    best_idx[o] = bi;
+    if (blk_max) { best_lg[o] = bl; blk_max[o] = bmx; blk_sum[o] = sh[6] + sh[7]; }
+  }
+}
+
+// logits[m][n] = sum_s parts[s][m][n]; per (m, block of 128 columns) the pick rule.
 __global__ __launch_bounds__(128) void reduce_argmax_kernel(const float* __restrict__ parts, int S,
                                                             int M, int N, float* __restrict__ logits,
                                                             float* __restrict__ best_val,
-                                                            int32_t* __restrict__ best_idx,
-                                                            int nb, int32_t* __restrict__ bump) {
-  __shared__ float sv[2];
-  __shared__ int si[2];
+                                                            int32_t* __restrict__ best_idx, int nb,
+                                                            const int32_t* __restrict__ pos_dev,
+                                                            int32_t* __restrict__ pos_next, SampleArgs smp) {
+  __shared__ float sh[8];
+  __shared__ int shi[2];
   const int m = blockIdx.y, n = blockIdx.x * 128 + threadIdx.x;
   const size_t total = (size_t)M * N;
-  float v = -INFINITY;
-  int idx = min(blockIdx.x * 128, N - 1);
+  float a = 0.f;
   if (n < N) {
-    float a = 0.f;
     for (int s = 0; s < S; ++s) a += parts[(size_t)s * total + (size_t)m * N + n];
     if (logits) logits[(size_t)m * N + n] = a;
-    v = a;
-    idx = n;
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(idx, o, 64);
-    if (gv_better(ov, oi, v, idx)) { v = ov; idx = oi; }
-  }
-  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = v; si[threadIdx.x >> 6] = idx; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (gv_better(sv[1], si[1], v, idx)) { v = sv[1]; idx = si[1]; }
-    best_val[(size_t)m * nb + blockIdx.x] = v;
-    best_idx[(size_t)m * nb + blockIdx.x] = idx;
-    if (bump && blockIdx.x == 0 && m == 0) *bump += 1;
-  }
+  const int gpos = pos_dev ? *pos_dev + 1 : 0;
+  pick_block128(n < N, a, n, m, nb, smp.inv_temp, smp.seed, gpos, best_val, best_idx, smp.best_lg,
+                smp.blk_max, smp.blk_sum, sh, shi);
+  if (pos_next && blockIdx.x == 0 && m == 0 && threadIdx.x == 0) *pos_next = gpos;
 }
 
 void launch_reduce_relu(const float* parts, int S, const void* bias, void* out, int M, int N, int mt,
@@ -394,9 +451,11 @@ void launch_reduce_relu(const float* parts, int S, const void* bias, void* out, 
 }
 
 void launch_reduce_argmax(const float* parts, int S, int M, int N, float* logits, float* best_val,
-                          int32_t* best_idx, int nb, int32_t* bump, hipStream_t st) {
+                          int32_t* best_idx, int nb, const int32_t* pos_dev, int32_t* pos_next,
+                          const SampleArgs& smp, hipStream_t st) {
   dim3 grid((N + 127) / 128, M);
-  reduce_argmax_kernel<<<grid, 128, 0, st>>>(parts, S, M, N, logits, best_val, best_idx, nb, bump);
+  reduce_argmax_kernel<<<grid, 128, 0, st>>>(parts, S, M, N, logits, best_val, best_idx, nb, pos_dev,
+                                             pos_next, smp);
 }
 
 // ---------------------------------------------------------------------------------
@@ -406,8 +465,8 @@ template <int OUT>
 __global__ __launch_bounds__(128) void gemv_f32_kernel(const float* __restrict__ X,
                                                        const float* __restrict__ W, int M, int N,
                                                        int K, GemvArgs g) {
-  __shared__ float sv[2];
-  __shared__ int si[2];
+  __shared__ float sh[8];
+  __shared__ int shi[2];
   const int n = blockIdx.x * 128 + threadIdx.x;
   const int m = blockIdx.z;
   const int s0 = (int)((long)blockIdx.y * K / gridDim.y), s1 = (int)((long)(blockIdx.y + 1) * K / gridDim.y);
@@ -418,24 +477,12 @@ __global__ __launch_bounds__(128) void gemv_f32_kernel(const float* __restrict__
     if (n < N) g.parts[((size_t)blockIdx.y * M + m) * N + n] = acc;
   } else if (OUT == GV_RELU) {
     if (n < N) ((float*)g.out)[(size_t)m * N + n] = fmaxf(acc + ((const float*)g.bias)[n], 0.f);
-  } else {
+  } else {   // one split (the whole K): the pick rule per 128-column block
     if (n < N && g.logits) g.logits[(size_t)m * N + n] = acc;
-    float bv = n < N ? acc : -INFINITY;
-    int bi = n < N ? n : N - 1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (gv_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      if (gv_better(sv[1], si[1], bv, bi)) { bv = sv[1]; bi = si[1]; }
-      g.best_val[(size_t)m * g.n_blocks + blockIdx.x] = bv;
-      g.best_idx[(size_t)m * g.n_blocks + blockIdx.x] = bi;
-      if (g.bump && blockIdx.x == 0 && m == 0) *g.bump += 1;
-    }
+    const int gpos = g.pos_dev ? *g.pos_dev + 1 : 0;
+    pick_block128(n < N, acc, n, m, g.n_blocks, g.smp.inv_temp, g.smp.seed, gpos, g.best_val, g.best_idx,
+                  g.smp.best_lg, g.smp.blk_max, g.smp.blk_sum, sh, shi);
+    if (g.pos_next && blockIdx.x == 0 && m == 0 && threadIdx.x == 0) *g.pos_next = gpos;
   }
 }
 
@@ -446,7 +493,9 @@ void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, cons
     a.M = M; a.N = N; a.K = K; a.il = g.w_il; a.ns = p.kr / 32;
     a.parts = g.parts; a.bias = (const bf16*)g.bias; a.out = (bf16*)g.out;
     a.logits = g.logits; a.best_val = g.best_val; a.best_idx = g.best_idx;
-    a.n_blocks = g.n_blocks; a.bump = g.bump;
+    a.n_blocks = g.n_blocks; a.pos_next = g.pos_next;
+    a.inv_temp = g.smp.inv_temp; a.seed = g.smp.seed;
+    a.best_lg = g.smp.best_lg; a.blk_max = g.smp.blk_max; a.blk_sum = g.smp.blk_sum;
     a.q_out = (bf16*)g.q_out; a.k_cache = (bf16*)g.k_cache; a.v_cache = (bf16*)g.v_cache;
     a.pos_dev = g.pos_dev; a.d = g.d; a.H = g.H; a.D = g.D; a.S_max = g.S_max; a.q_scale = g.q_scale;
     const bf16* x = (const bf16*)X;

@@ -108,6 +108,21 @@ struct GemvPlan {
 int decode_mt(int M);
 GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole = false);
 
+// Pick rule of the LM head.  inv_temp == 0: greedy (largest logit, lowest index on
+// ties).  inv_temp > 0: the Gumbel-max sample of softmax(logit * inv_temp): largest
+// logit * inv_temp + G, G from gumbel4 (common.h) with this seed, the batch row and
+// the position of the token being generated.  Per (row, column block) the head also
+// reports, when blk_max is set, the tempered logit (logit * max(inv_temp, 1 if 0)) of
+// the block's pick, the block's largest tempered logit and the sum of
+// exp(tempered logit - that maximum), from which the token's log-probability follows.
+struct SampleArgs {
+  float inv_temp = 0.f;
+  uint64_t seed = 0;
+  float* best_lg = nullptr;       // [M][n_blocks]
+  float* blk_max = nullptr;       // [M][n_blocks]
+  float* blk_sum = nullptr;       // [M][n_blocks]
+};
+
 struct GemvArgs {
   int out_mode = GV_PARTIAL;
   int w_il = 0;                   // bf16 W: 0 row-major, else the inference layout il_of(K)
@@ -118,8 +133,10 @@ struct GemvArgs {
   float* best_val = nullptr;      // GV_ARGMAX: [M][n_blocks] per-block maxima
   int32_t* best_idx = nullptr;    // GV_ARGMAX: [M][n_blocks]
   int n_blocks = 0;               // GV_ARGMAX: gemv_argmax_blocks(dt, plan, N)
-  int32_t* bump = nullptr;        // GV_ARGMAX: if set, *bump += 1 once (the decode
-                                  // position; this kernel never reads it)
+  // GV_ARGMAX: the token being picked sits at position *pos_dev + 1 (pos_dev as for
+  // GV_QKV, read only); that value is stored to *pos_next (for launch_argmax_finalize)
+  int32_t* pos_next = nullptr;
+  SampleArgs smp;
   // GV_QKV (bf16, plan.splits == 1): rows n of the packed [q; k; v] projection plus
   // bias; q scaled and rounded into q_out [M][d], k and v rounded and appended to
   // the layer's cache [B_max][H][S_max][D] at position *pos_dev
@@ -144,17 +161,22 @@ int gemv_argmax_blocks(int dt, const GemvPlan& p, int N);
 void launch_reduce_relu(const float* parts, int S, const void* bias, void* out, int M, int N,
                         int mt, hipStream_t st);
 // Sum S partial logits, optionally store them, and reduce each row's 128-column
-// blocks to (max, lowest index) pairs for launch_argmax_finalize; *bump += 1 once.
+// blocks to (pick value, lowest index) pairs under the rule `smp` for
+// launch_argmax_finalize; the token sits at *pos_dev + 1, stored to *pos_next.
 void launch_reduce_argmax(const float* parts, int S, int M, int N, float* logits, float* best_val,
-                          int32_t* best_idx, int nb, int32_t* bump, hipStream_t st);
+                          int32_t* best_idx, int nb, const int32_t* pos_dev, int32_t* pos_next,
+                          const SampleArgs& smp, hipStream_t st);
 
-// Reduce per-block argmax partials: pick[m] = lowest index among the maxima.
-// Writes pick to ids_cur[m], tokens[m * tok_stride + *pos_dev] (if tokens; the
-// LM-head launch has already advanced the position, so this is the slot of the
-// token being picked) and d_next[m] (if non-null).
-void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, int n_blocks, int M,
-                            int32_t* ids_cur, int32_t* tokens, int tok_stride,
-                            const int32_t* pos_dev, int32_t* d_next, hipStream_t st);
+// Reduce per-block partials: pick[m] = lowest index among the block maxima.  p =
+// *pos_next is the position of the token being picked.  Writes pick to ids_cur[m],
+// tokens[m * tok_stride + p] (if tokens) and d_next[m] (if non-null); with logp (and
+// smp's block sums), the pick's log-probability to logp[m * tok_stride + p]: the
+// tempered logit minus the logsumexp of the row, blocks combined in a fixed order.
+// Finally *pos_dev = p (the position the next step feeds).
+void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, const SampleArgs& smp,
+                            int n_blocks, int M, int32_t* ids_cur, int32_t* tokens, float* logp,
+                            int tok_stride, const int32_t* pos_next, int32_t* pos_dev, int32_t* d_next,
+                            hipStream_t st);
 
 // ---- attention ---------------------------------------------------------------------
 // Causal attention of the prompt pass: q [B*S, d] (scaled), keys/values of

@@ -55,6 +55,10 @@ class he_lora_table(ctypes.Structure):
     _fields_ = [("rank", _i32), ("alpha", ctypes.c_float), ("pairs", ctypes.POINTER(he_lora_pair))]
 
 
+class he_sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("seed", ctypes.c_uint64)]
+
+
 class he_kernel_stat(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
                 ("bytes", ctypes.c_double), ("flops", ctypes.c_double)]
@@ -73,6 +77,7 @@ _SIGS = {
     "he_prefill": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "he_decode_step": (_i32, [_vp, _vp, _vp, _vp]),
     "he_generate": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
+    "he_generate_ex": (_i32, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
     "he_score": (_i32, [_vp, _vp, _i32, _i32, _vp]),
     "he_sync": (_i32, [_vp]),
     "he_last_error": (ctypes.c_char_p, [_vp]),
@@ -151,6 +156,12 @@ def he_decode_step(ctx, d_in: int, d_next: int, d_logits: int = 0):
 
 def he_generate(ctx, d_prompt: int, B: int, S: int, S_g: int, d_out: int):
     return _check(lib().he_generate(ctx, _vp(d_prompt), B, S, S_g, _vp(d_out)), ctx)
+
+
+def he_generate_ex(ctx, d_prompt: int, B: int, S: int, S_g: int, smp, d_out: int, d_logprobs: int = 0):
+    """smp: he_sampling or None (greedy)."""
+    p = ctypes.byref(smp) if smp is not None else None
+    return _check(lib().he_generate_ex(ctx, _vp(d_prompt), B, S, S_g, p, _vp(d_out), _vp(d_logprobs or None)), ctx)
 
 
 def he_score(ctx, d_ids: int, B: int, S: int, d_reward: int):
