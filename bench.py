@@ -443,6 +443,45 @@ def main():
             "mean_logprob": float(lps.mean()), "logprobs_finite": bool((lps == lps).all())}
         log(f"sampled: {json.dumps(res['sampled'])}")
 
+        # teacher-forced scoring of the finished experience (prompt + the answer just
+        # sampled, S + G tokens): log-probabilities of the B x G answer tokens, fused weights
+        with torch.cuda.stream(st):
+            seq = torch.cat([prompts, out], dim=1).contiguous()
+            lpt = torch.empty(B, G, dtype=torch.float32, device="cuda")
+            E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            he.he_fuse_lora(ctx, lt)
+            he.he_logprobs(ctx, seq.data_ptr(), B, S + G, S, lpt.data_ptr())
+            E[0].record(st)
+            for _ in range(2):
+                he.he_logprobs(ctx, seq.data_ptr(), B, S + G, S, lpt.data_ptr())
+            E[1].record(st)
+            cls = {"gemm": he.HE_K_GEMM_PREFILL, "attn": he.HE_K_ATTN_PREFILL, "vocab": he.HE_K_VOCAB}
+            for k in cls.values():
+                he.he_kernel_timer(ctx, k, True)
+            he.he_logprobs(ctx, seq.data_ptr(), B, S + G, S, lpt.data_ptr())
+            cs = {n: he.he_kernel_stats(ctx, k) for n, k in cls.items()}
+            for k in cls.values():
+                he.he_kernel_timer(ctx, k, False)
+            he.he_unfuse_lora(ctx, lt)
+            he.he_sync(ctx)
+            torch.cuda.synchronize()
+        t_sc = E[0].elapsed_time(E[1]) / 1e3 / 2
+        T = S + G
+        L, d, F, V = a.n_layers, a.d_model, a.d_ffn, a.vocab
+        sc_flops = (2.0 * B * T * L * (4 * d * d + 2 * d * F) + 2.0 * L * d * T * (T + 1) * B
+                    + 2.0 * B * G * d * V)
+        lpv = lpt.cpu().numpy()
+        tf = lambda st_: st_.flops / (st_.total_ms / 1e3) / 1e12 if st_.total_ms else None
+        res["scoring"] = {
+            "sequence": T, "prompt_len": S, "answer_len": G, "ms": t_sc * 1e3,
+            "scored_tokens_per_s": B * G / t_sc, "TFLOPs": sc_flops / t_sc / 1e12,
+            "mfma_frac": sc_flops / t_sc / BF16_PEAK,
+            "layer_gemm_ms": cs["gemm"].total_ms, "layer_gemm_TFLOPs": tf(cs["gemm"]),
+            "attn_ms": cs["attn"].total_ms,
+            "vocab_ms": cs["vocab"].total_ms, "vocab_TFLOPs": tf(cs["vocab"]),
+            "mean_logprob": float(lpv.mean()), "logprobs_finite": bool(((lpv == lpv) & (abs(lpv) < float("inf"))).all())}
+        log(f"scoring: {json.dumps(res['scoring'])}")
+
     with torch.cuda.stream(st):
         he.he_release_cache(ctx)
         he.he_sync(ctx)

@@ -271,6 +271,23 @@ he_status he_generate_ex(he_ctx* ctx, const int32_t* d_prompt, int32_t B, int32_
  * Errors: HE_E_NOCACHE, HE_E_ARG, HE_E_RANGE, HE_E_UNSUPPORTED (LM-head model). */
 he_status he_score(he_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t S, float* d_reward);
 
+/* Teacher-forced scoring of finished experience (page 1, pipeline section: the PPO
+ * step needs, for every answer token, its log-probability under the actor and under
+ * the frozen reference model).  d_seq [B, S] int32 holds each row's prompt
+ * (positions 0 .. S_p-1) followed by its answer; d_logprobs [B, S - S_p] float32
+ * receives, for j = 0 .. S-S_p-1, log softmax(logits at position S_p-1+j)[seq[S_p+j]]:
+ * the log-probability of answer token j given everything before it, at temperature
+ * 1, the row's logsumexp merged in a fixed order.  One causal prompt pass over all S
+ * positions (the KV cache is overwritten; a following he_decode_step needs a new
+ * prefill), the final LayerNorm of the S - S_p scored positions, and the tied head in
+ * chunks of at most 4096 rows of fp32 logits held in the workspace.  Device memory,
+ * caller-owned, written by the end of the call's stream work; a target id outside
+ * 0 .. vocab-1 yields NaN for that position.
+ * Errors: HE_E_NOCACHE, HE_E_ARG (NULL buffer, batch outside 1..max_batch, S_p
+ * outside 1..S-1), HE_E_RANGE (S > max_seq), HE_E_UNSUPPORTED (not an LM-head model). */
+he_status he_logprobs(he_ctx* ctx, const int32_t* d_seq, int32_t B, int32_t S, int32_t S_p,
+                      float* d_logprobs);
+
 /* Wait for the context's stream; reports deferred device faults as HE_E_HIP. */
 he_status he_sync(he_ctx* ctx);
 
@@ -295,6 +312,7 @@ enum {
   HE_K_ATTN_DECODE,
   HE_K_LMHEAD,
   HE_K_SCORE,
+  HE_K_VOCAB,
   HE_K_COUNT
 };
 

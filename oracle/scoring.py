@@ -35,7 +35,12 @@ def teacher_forced_logprobs(model: O.OracleModel, seq, prompt_len: int) -> np.nd
     if not 1 <= prompt_len < S:
         raise ValueError("need 1 <= prompt_len < S")
     h = model.hidden(seq, 0, None)[:, prompt_len - 1:S - 1]        # predicts tokens prompt_len .. S-1
-    logits = model.lm_logits(h)                                     # [B, n, V]
-    target = seq[:, prompt_len:]
+    return logprobs_from_logits(model.lm_logits(h), seq[:, prompt_len:])
+
+
+def logprobs_from_logits(logits, target) -> np.ndarray:
+    """log softmax(logits)[target] along the last axis: logits [..., V], target [...]."""
+    logits = np.asarray(logits, dtype=np.float64)
+    target = np.asarray(target).astype(np.int64)
     picked = np.take_along_axis(logits, target[..., None], axis=-1)[..., 0]
     return picked - logsumexp(logits, axis=-1)

@@ -30,7 +30,8 @@ def _declared():
 def test_exports_every_declared_call():
     names = _declared()
     assert "he_generate" in names and "he_generate_ex" in names and "he_fuse_lora" in names
-    assert len(names) >= 18
+    assert "he_logprobs" in names
+    assert len(names) >= 19
     L = ctypes.CDLL(he.LIB_PATH)
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
@@ -152,6 +153,13 @@ def test_argument_checks():
     he.he_generate_ex(ctx, P, 2, 16, 8, he.he_sampling(0.7, 123), P, 0)
     assert _status(he.he_generate_ex, ctx, P, 2, 16, 18, he.he_sampling(1.0, 1), P, P) == he.HE_E_RANGE
     assert _status(he.he_generate_ex, ctx, 0, 2, 16, 8, he.he_sampling(1.0, 1), P, P) == he.HE_E_ARG
+    # teacher-forced scoring: 1 <= S_p < S <= max_seq, buffers non-NULL
+    he.he_logprobs(ctx, P, 2, 32, 16, P)
+    he.he_logprobs(ctx, P, 1, 2, 1, P)
+    for args, st in (((P, 2, 32, 0, P), he.HE_E_ARG), ((P, 2, 32, 32, P), he.HE_E_ARG),
+                     ((P, 2, 33, 16, P), he.HE_E_RANGE), ((P, 3, 32, 16, P), he.HE_E_ARG),
+                     ((0, 2, 32, 16, P), he.HE_E_ARG), ((P, 2, 32, 16, 0), he.HE_E_ARG)):
+        assert _status(he.he_logprobs, ctx, *args) == st, args
     bad = he.he_lora_table(rank=0, alpha=1.0, pairs=(he.he_lora_pair * 12)())
     assert _status(he.he_fuse_lora, ctx, bad) == he.HE_E_ARG
     assert "rank" in he.he_last_error(ctx)
@@ -210,5 +218,6 @@ def test_reward_model_only_scores():
     he.he_retake_cache(ctx, 128, 512)
     he.he_score(ctx, P, 128, 512, P)
     assert _status(he.he_prefill, ctx, P, 2, 16, P) == he.HE_E_UNSUPPORTED
+    assert _status(he.he_logprobs, ctx, P, 2, 16, 8, P) == he.HE_E_UNSUPPORTED
     assert _status(he.he_score, ctx, P, 129, 512, P) == he.HE_E_ARG
     e.close()

@@ -9,16 +9,24 @@ import torch
 
 import synth
 from oracle import opt_he as O
+from oracle import scoring as SC
 from transformer_decode_amd import he
 
-from gpu_util import GpuRun, check_logits, greedy_prefix_agrees, log, oracle_floor, precision, to_dev
+from gpu_util import (BF16_ABS_TOL, FLOOR_FACTOR, GpuRun, check_logits, greedy_prefix_agrees, log,
+                      oracle_floor, precision, to_dev)
 
 pytestmark = pytest.mark.gpu
 
 
 def _sampled_teacher_forced(wl, rows, steps):
     """Full batch on the GPU (prefill + 255 forced steps, graph replay); the oracle
-    recomputes the sampled rows from scratch (definition mode, no cache)."""
+    recomputes the sampled rows from scratch (definition mode, no cache).  Then the
+    scoring pass (he_logprobs) over the full batch of prompt + 256 forced tokens, the
+    workload's own 512-token experience, checked on the same rows at every answer
+    position: its log-probabilities need the oracle's logits at positions
+    prompt_len - 1 .. prompt_len + 254, which the definition-mode pass already has.
+    Bound: twice the row's logit bound (the larger of 3e-2 and 1.5 x the oracle's
+    measured self-sensitivity over its recorded steps)."""
     log(f"{wl.name}: inputs")
     params = synth.model_params(wl.actor)
     lora = synth.lora_params(wl.actor, wl.lora_rank)
@@ -30,6 +38,15 @@ def _sampled_teacher_forced(wl, rows, steps):
         he.he_retake_cache(run.ctx, wl.batch, wl.max_seq)
     log(f"{wl.name}: GPU teacher-forced run")
     got = run.teacher_forced(prompts, forced, wl.gen_len, want_rows=rows, want_steps=set(steps))
+    log(f"{wl.name}: GPU scoring pass")
+    B, S_p, n = wl.batch, wl.prompt_len, wl.gen_len
+    exp = torch.cat([prompts, forced], dim=1).to(torch.int32).cuda()
+    lp = torch.full((B, n), float("nan"), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(run.stream):
+        he.he_logprobs(run.ctx, exp.data_ptr(), B, S_p + n, S_p, lp.data_ptr())
+        he.he_sync(run.ctx)
+    lp = lp.cpu().numpy()
+    assert np.isfinite(lp).all()
     run.close()
     del run
     torch.cuda.empty_cache()
@@ -45,6 +62,13 @@ def _sampled_teacher_forced(wl, rows, steps):
         floors = [oracle_floor(wl.name, r, j) for r in rows]
         worst = max(worst, check_logits(got[j], full[:, S - 1 + j], wl.actor, f"{wl.name} step {j}", floors))
     log(f"{wl.name}: max |dlogit| {worst:.3e}")
+    want = SC.logprobs_from_logits(full[:, S - 1:S - 1 + n], forced.numpy()[rows, :n])
+    for i, r in enumerate(rows):
+        fl = [oracle_floor(wl.name, r, j) for j in steps]
+        bound = 2 * max([BF16_ABS_TOL] + [FLOOR_FACTOR * f for f in fl if f is not None])
+        err = np.abs(lp[r].astype(np.float64) - want[i])
+        log(f"{wl.name} scoring row {r}: {n} log-probs, max |d| {err.max():.3e} (bound {bound:.2e})")
+        assert err.max() <= bound, f"row {r}: max |dlogprob| {err.max():.3e} at answer token {err.argmax()}"
 
 
 def test_opt1_3b_sampled_rows():

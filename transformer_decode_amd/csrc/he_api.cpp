@@ -34,6 +34,7 @@ using namespace he;
 namespace {
 
 constexpr int kMaxDecodeBatch = 128;   // decode GEMM keeps <= 8 MFMA column tiles
+constexpr size_t kLogitChunk = 4096;   // vocabulary rows the scoring pass holds at once
 
 struct Timer {
   bool armed = false;
@@ -86,6 +87,8 @@ struct he_ctx {
   float* blk_max = nullptr;       // the block's largest tempered logit and its sum of
   float* blk_sum = nullptr;       // exponentials
   int n_argmax_blocks = 0, argmax_cap = 0;
+  float* lgc = nullptr;           // [lg_rows][V] fp32 logits of the scoring pass, one chunk
+  int lg_rows = 0;
   // pick rule of the LM head: temperature 0 greedy, else Gumbel-max sampling; and
   // whether log-probabilities are formed
   float inv_temp = 0.f;
@@ -299,8 +302,9 @@ static void enqueue_lm_head(he_ctx* c, int B, bool want_logits) {
                          c->want_logp ? c->logp : nullptr, c->max_seq + 1, c->pos_next, c->pos_dev, nullptr, st);
 }
 
-// Prompt pass of a pre-LN LM-head model; leaves z (final LN of the last rows) in x.
-static void enqueue_prefill_lm(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
+// Decoder layers of the prompt pass of a pre-LN LM-head model over ids [B, S]: leaves
+// the residual stream in h and every position's K/V in the cache.
+static void enqueue_prompt_layers(he_ctx* c, const int32_t* ids, int B, int S) {
   const int M = B * S, d = c->d, F = c->F, dt = c->dt;
   const float eps = c->desc.ln_eps;
   const size_t es = esize(dt);
@@ -348,6 +352,15 @@ static void enqueue_prefill_lm(he_ctx* c, const int32_t* ids, int B, int S, bool
                     eps, c->x, M, d, 1, 0, 0, -ald, st);
       });
   }
+}
+
+// Prompt pass; leaves z (final LN of the last rows) in x and picks the first token.
+static void enqueue_prefill_lm(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
+  const int d = c->d, dt = c->dt;
+  const float eps = c->desc.ln_eps;
+  const size_t es = esize(dt);
+  hipStream_t st = c->stream;
+  enqueue_prompt_layers(c, ids, B, S);
   // final LayerNorm of the last prompt position only, laid out for the LM head
   run_k(c, HE_K_EMBED_NORM, (double)B * d * (4 + es), 0, [&] {
     launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, S, S - 1, 0,
@@ -714,6 +727,9 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   const size_t o_bsm = take((size_t)bpad * argmax_cap * 4);
   const size_t o_pos = take(256);
   const size_t o_posn = take(256);
+  // one chunk of scoring-pass logits: up to kLogitChunk rows of the vocabulary
+  const int lg_rows = c->desc.head == HE_HEAD_LM ? (int)std::min<size_t>(rows, kLogitChunk) : 0;
+  const size_t o_lgc = take((size_t)lg_rows * c->V * 4);
   c->max_batch = max_batch;
   c->max_seq = max_seq;
   c->bpad = bpad;
@@ -758,6 +774,8 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   c->best_lg = (float*)(scratch + o_blg);
   c->blk_max = (float*)(scratch + o_bmx);
   c->blk_sum = (float*)(scratch + o_bsm);
+  c->lgc = (float*)(scratch + o_lgc);
+  c->lg_rows = lg_rows;
   c->cache = true;
   c->prefilled = false;
   // The decode GEMM reads X rows up to the next multiple of 16: give the padding
@@ -940,6 +958,46 @@ he_status he_generate_ex(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t 
   c->seed = smp && t > 0.f ? smp->seed : 0;
   c->want_logp = d_logprobs != nullptr;
   return generate(c, d_prompt, B, S, S_g, d_out, d_logprobs);
+}
+
+// Teacher-forced scoring: prompt pass over the whole sequence, final LayerNorm of the
+// positions S_p - 1 .. S - 2 of every row (each predicts the next token), then in
+// chunks of lg_rows rows the tied-head GEMM into fp32 logits and the log-softmax gather.
+static void enqueue_logprobs(he_ctx* c, const int32_t* seq, int B, int S, int S_p, float* out) {
+  const int d = c->d, dt = c->dt, n = S - S_p, Mp = B * n;
+  const float eps = c->desc.ln_eps;
+  const size_t es = esize(dt);
+  hipStream_t st = c->stream;
+  enqueue_prompt_layers(c, seq, B, S);
+  const int ald = a_il(c, d);
+  run_k(c, HE_K_EMBED_NORM, (double)Mp * d * (4 + es), 0, [&] {
+    launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, Mp, d, S, S_p - 1, 0,
+                -ald, st, n);
+  });
+  for (int r0 = 0; r0 < Mp; r0 += c->lg_rows) {
+    const int mc = std::min(c->lg_rows, Mp - r0);
+    EpiArgs e;
+    e.mode = EPI_F32;
+    e.out_f32 = c->lgc;
+    e.w_il = e_il(c);
+    e.x_il = ald;
+    const char* xr = (const char*)c->x + (size_t)r0 * d * es;   // r0 % 16 == 0: whole row blocks
+    run_k(c, HE_K_VOCAB, (double)c->V * d * es + (double)mc * c->V * 8, 2.0 * mc * c->V * d, [&] {
+      launch_gemm(dt, xr, c->wt.tok_emb, mc, c->V, d, e, st);
+      launch_logprob_gather(c->lgc, mc, c->V, seq, S, S_p, n, r0, out, st);
+    });
+  }
+}
+
+he_status he_logprobs(he_ctx* c, const int32_t* d_seq, int32_t B, int32_t S, int32_t S_p, float* d_logprobs) {
+  if (!c) return HE_E_ARG;
+  he_status s = prefill_checks(c, d_seq, B, S, d_logprobs);
+  if (s != HE_OK) return s;
+  if (S_p < 1 || S_p >= S) return set_err(c, HE_E_ARG, "prompt length %d outside 1..%d", S_p, S - 1);
+  c->prefilled = false;   // the cache now holds the scored sequences
+  if (c->validate_only) return HE_OK;
+  enqueue_logprobs(c, d_seq, B, S, S_p, d_logprobs);
+  return check_launch(c, "logprobs launch");
 }
 
 he_status he_score(he_ctx* c, const int32_t* d_ids, int32_t B, int32_t S, float* d_reward) {

@@ -344,10 +344,10 @@ __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
                                                     const T* __restrict__ g,
                                                     const T* __restrict__ b, float eps,
                                                     T* __restrict__ x, int M, int d, int row_stride,
-                                                    int row_offset, int post, int x_lay) {
+                                                    int row_offset, int post, int x_lay, int row_group) {
   __shared__ float red[64];
   const int r = blockIdx.x, tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
-  const size_t row = (size_t)r * row_stride + row_offset;
+  const size_t row = (size_t)(r / row_group) * row_stride + row_offset + r % row_group;
   float* hr = h + row * d;
   float v[kLnChunks][4];
 #pragma unroll
@@ -388,16 +388,78 @@ __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
 
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias, const void* g,
                  const void* b, float eps, void* x, int M, int d, int row_stride, int row_offset,
-                 int post, int x_lay, hipStream_t st) {
+                 int post, int x_lay, hipStream_t st, int row_group) {
   const int nt = ln_threads(d);
   if (dt == DT_BF16)
     norm_kernel<bf16><<<M, nt, 0, st>>>(h, parts, nsplit, (const bf16*)bias, (const bf16*)g,
                                         (const bf16*)b, eps, (bf16*)x, M, d, row_stride, row_offset, post,
-                                        x_lay);
+                                        x_lay, row_group);
   else
     norm_kernel<float><<<M, nt, 0, st>>>(h, parts, nsplit, (const float*)bias, (const float*)g,
                                          (const float*)b, eps, (float*)x, M, d, row_stride, row_offset, post,
-                                         0);
+                                         0, row_group);
+}
+
+// ---------------------------------------------------------------------------------
+// teacher-forced log-probabilities
+// ---------------------------------------------------------------------------------
+// (m, s) pairs stand for s * exp(m): the running maximum and the sum of exp(l - m).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mx = fmaxf(m, m2);
+  if (mx == -INFINITY) return;                     // both empty
+  s = s * expf(m - mx) + s2 * expf(m2 - mx);
+  m = mx;
+}
+
+__global__ __launch_bounds__(256) void logprob_gather_kernel(const float* __restrict__ logits, int V,
+                                                             const int32_t* __restrict__ seq, int S,
+                                                             int S_p, int n, int r0,
+                                                             float* __restrict__ out) {
+  __shared__ float sm[256], ss[256];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int g = r0 + r, b = g / n, j = g - b * n;
+  const float* L = logits + (size_t)r * V;
+  float m = -INFINITY, s = 0.f;
+  const int V4 = (V & 3) == 0 ? V >> 2 : 0;        // rows are 16-byte aligned when V % 4 == 0
+  for (int i = tid; i < V4; i += 256) {
+    const float4 v = reinterpret_cast<const float4*>(L)[i];
+    const float mx = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    if (mx > m) {
+      s *= expf(m - mx);
+      m = mx;
+    }
+    s += (expf(v.x - m) + expf(v.y - m)) + (expf(v.z - m) + expf(v.w - m));
+  }
+  for (int i = 4 * V4 + tid; i < V; i += 256) {
+    const float x = L[i];
+    if (x > m) {
+      s *= expf(m - x);
+      m = x;
+    }
+    s += expf(x - m);
+  }
+  sm[tid] = m;
+  ss[tid] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {             // fixed tree: thread t takes t + w
+    if (tid < w) {
+      float a = sm[tid], c = ss[tid];
+      lse_merge(a, c, sm[tid + w], ss[tid + w]);
+      sm[tid] = a;
+      ss[tid] = c;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int t = seq[(size_t)b * S + S_p + j];
+    out[g] = (t >= 0 && t < V) ? L[t] - (sm[0] + logf(ss[0])) : __int_as_float(0x7fc00000);
+  }
+}
+
+void launch_logprob_gather(const float* logits, int rows, int V, const int32_t* seq, int S, int S_p,
+                           int n, int r0, float* out, hipStream_t st) {
+  if (rows <= 0) return;
+  logprob_gather_kernel<<<rows, 256, 0, st>>>(logits, V, seq, S, S_p, n, r0, out);
 }
 
 // ---------------------------------------------------------------------------------

@@ -57,9 +57,12 @@ void launch_embed_gather(int dt, const int32_t* ids, const void* E, void* xe, in
 //   post == 0: x[r] = round(LN(h[row]))             (pre-LN: h untouched by the norm)
 //   post == 1: h[row] = LN(h[row]); x[r] = round(h[row])  (post-LN)
 //   x_lay:   layout of x as for launch_embed_norm (act_off)
+//   row_group: output rows come in groups of row_group consecutive stream rows: row r
+//      reads stream row (r / row_group) * row_stride + row_offset + r % row_group
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias,
                  const void* g, const void* b, float eps, void* x, int M, int d,
-                 int row_stride, int row_offset, int post, int x_lay, hipStream_t st);
+                 int row_stride, int row_offset, int post, int x_lay, hipStream_t st,
+                 int row_group = 1);
 
 // ---- GEMM epilogues ------------------------------------------------------------
 enum Epi { EPI_QKV = 0, EPI_RESID, EPI_RELU, EPI_POSADD, EPI_F32 };
@@ -177,6 +180,14 @@ void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, cons
                             int n_blocks, int M, int32_t* ids_cur, int32_t* tokens, float* logp,
                             int tok_stride, const int32_t* pos_next, int32_t* pos_dev, int32_t* d_next,
                             hipStream_t st);
+
+// Teacher-forced log-probabilities from fp32 logits [rows][V] (row-major): chunk row
+// r is scored row g = r0 + r, i.e. sequence b = g / n, answer token j = g % n, whose
+// target is seq[b * S + S_p + j]; out[g] = logits[r][target] - logsumexp(logits[r]),
+// the logsumexp merged over the threads' column slices in a fixed tree.  A target
+// outside 0 .. V-1 gives NaN.
+void launch_logprob_gather(const float* logits, int rows, int V, const int32_t* seq, int S, int S_p,
+                           int n, int r0, float* out, hipStream_t st);
 
 // ---- attention ---------------------------------------------------------------------
 // Causal attention of the prompt pass: q [B*S, d] (scaled), keys/values of

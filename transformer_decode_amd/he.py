@@ -22,7 +22,7 @@ HE_HEAD_LM, HE_HEAD_SCALAR = 0, 1
 HE_FLAG_VALIDATE_ONLY = 1
 HE_PROJ_Q, HE_PROJ_K, HE_PROJ_V, HE_PROJ_OUT, HE_PROJ_FC1, HE_PROJ_FC2, HE_N_PROJ = range(7)
 (HE_K_LORA, HE_K_EMBED_NORM, HE_K_GEMM_PREFILL, HE_K_ATTN_PREFILL, HE_K_GEMV_DECODE,
- HE_K_ATTN_DECODE, HE_K_LMHEAD, HE_K_SCORE, HE_K_COUNT) = range(9)
+ HE_K_ATTN_DECODE, HE_K_LMHEAD, HE_K_SCORE, HE_K_VOCAB, HE_K_COUNT) = range(10)
 HE_DBG_FAIL_NEXT_ALLOC, HE_DBG_FAIL_NEXT_STEP = 1, 2
 
 _vp = ctypes.c_void_p
@@ -79,6 +79,7 @@ _SIGS = {
     "he_generate": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "he_generate_ex": (_i32, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
     "he_score": (_i32, [_vp, _vp, _i32, _i32, _vp]),
+    "he_logprobs": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "he_sync": (_i32, [_vp]),
     "he_last_error": (ctypes.c_char_p, [_vp]),
     "he_status_str": (ctypes.c_char_p, [_i32]),
@@ -166,6 +167,10 @@ def he_generate_ex(ctx, d_prompt: int, B: int, S: int, S_g: int, smp, d_out: int
 
 def he_score(ctx, d_ids: int, B: int, S: int, d_reward: int):
     return _check(lib().he_score(ctx, _vp(d_ids), B, S, _vp(d_reward)), ctx)
+
+
+def he_logprobs(ctx, d_seq: int, B: int, S: int, S_p: int, d_logprobs: int):
+    return _check(lib().he_logprobs(ctx, _vp(d_seq), B, S, S_p, _vp(d_logprobs)), ctx)
 
 
 def he_sync(ctx):
