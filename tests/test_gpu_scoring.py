@@ -123,3 +123,22 @@ def test_opt125m_scoring_reproduces_generation_logprobs(c2):
     _compare(b, a.astype(np.float64), 2 * BF16_LP_TOL, "opt125m generation vs scoring")
     # a token the model itself sampled is rarely very unlikely
     assert np.median(b) > -20
+
+
+def test_head_128_two_window_attention():
+    """Head size 128 with S = 400: the prompt-pass attention holds 256 keys of a head in
+    LDS at once, so queries past 256 run over two staged windows (the second ragged,
+    144 keys).  A two-layer bf16 model of that head size, every position scored."""
+    import dataclasses
+    shape = dataclasses.replace(C2.actor, n_layers=2, d_model=256, n_heads=2, d_ffn=512)
+    wl = dataclasses.replace(C2, name="head128", actor=shape, batch=2, max_seq=512)
+    params = synth.model_params(shape, seed=5)
+    lora = synth.lora_params(shape, wl.lora_rank, seed=5)
+    S_p, S = 100, 400
+    seq = _experience(wl, wl.prompt_len, wl.gen_len)[:, :S]
+    run = GpuRun(wl, params)
+    got = _gpu_logprobs(run, seq, S_p, lora_cpu=lora)
+    run.close()
+    om = O.OracleModel(shape, params, precision(shape), lora=lora, lora_scale=wl.lora_scale)
+    want = SC.teacher_forced_logprobs(om, seq.numpy(), S_p)
+    _compare(got, want, BF16_LP_TOL, "head 128, S = 400")

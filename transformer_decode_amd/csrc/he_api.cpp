@@ -982,8 +982,21 @@ static void enqueue_logprobs(he_ctx* c, const int32_t* seq, int B, int S, int S_
     e.w_il = e_il(c);
     e.x_il = ald;
     const char* xr = (const char*)c->x + (size_t)r0 * d * es;   // r0 % 16 == 0: whole row blocks
+    // bf16 chunks of whole 256-row tiles: the vocabulary's 256-column tiles on the
+    // fast GEMM, the remaining columns (a multiple of 16) on the general one
+    const int Nm = (dt == DT_BF16 && mc % 256 == 0 && d % 32 == 0) ? c->V / 256 * 256 : 0;
     run_k(c, HE_K_VOCAB, (double)c->V * d * es + (double)mc * c->V * 8, 2.0 * mc * c->V * d, [&] {
-      launch_gemm(dt, xr, c->wt.tok_emb, mc, c->V, d, e, st);
+      if (Nm) {
+        e.ldo = c->V;
+        launch_gemm(dt, xr, c->wt.tok_emb, mc, Nm, d, e, st);
+        if (Nm < c->V) {
+          EpiArgs t = e;
+          t.out_f32 = c->lgc + Nm;
+          launch_gemm(dt, xr, (const char*)c->wt.tok_emb + (size_t)Nm * d * es, mc, c->V - Nm, d, t, st);
+        }
+      } else {
+        launch_gemm(dt, xr, c->wt.tok_emb, mc, c->V, d, e, st);
+      }
       launch_logprob_gather(c->lgc, mc, c->V, seq, S, S_p, n, r0, out, st);
     });
   }

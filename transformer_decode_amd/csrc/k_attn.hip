@@ -408,17 +408,7 @@ __global__ __launch_bounds__(256) void attn_prefill_bf16_kernel(const bf16* __re
   }
 }
 
-// Prompt pass, bf16, K and V of one (sequence, head) resident in LDS.  One WG of 8
-// waves per (sequence, head): the head's keys go to LDS row-major and its values
-// transposed (64 KB each at most), once; then every wave works through 16-query
-// blocks with no further block barrier, taking blocks w and 15 - w of each 16 so the
-// causal work is even.  Scores are formed transposed, S^T = K Q^T, so each lane holds
-// four consecutive keys of one query: exactly the B operand of the 16 x 16 x 16 MFMA,
-// which then computes O^T = V^T P^T straight from registers.  Online softmax per 32
-// keys (running max, per-lane partial sums merged at the end); P enters the product
-// as bf16 high and low parts (p = hi + lo to ~16 bits).  Both LDS arrays are
-// XOR-swizzled by 16-byte chunk so the 16 lanes that read 16 keys (or 16 value rows)
-// at one offset hit distinct banks.
+// Prompt-pass attention with the keys and values of a head in LDS (below).
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ short bf_bits(bf16 v) { return (short)v; }
 // v combined with the v of lane l ^ 16 (row swap) or l ^ 32 (half swap), gfx950: the
@@ -441,45 +431,36 @@ __device__ __forceinline__ float sum32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 constexpr int kPfKV = 32768;           // bf16 elements of each of K and V^T in LDS
-// Keys padded for the LDS layout (a multiple of 128, at least 128), or 0 when the head
-// does not fit.
+// Key window held in LDS at once for head size D.
+constexpr int pf_window(int D) { return kPfKV / D; }
+// Keys padded for the LDS layout when the head fits in one window (a multiple of 128,
+// at least 128); the full window when it takes two; 0 when it does not fit in two.
 static int pf_pad(int S, int D) {
   const int sp = S <= 128 ? 128 : (S + 127) / 128 * 128;
-  return sp * D <= kPfKV ? sp : 0;
+  if (sp * D <= kPfKV) return sp;
+  return S <= 2 * pf_window(D) ? pf_window(D) : 0;
 }
 
+// Stage keys kw0 .. kw0 + Wp - 1 of one head (zeros past S) into the LDS arrays:
+// K row-major, key-local row `key`, chunk c at chunk c ^ ((key / RPB) mod NCH) of the
+// row; V transposed, row `dim` of Wp keys, chunk j (keys 8 j .. + 8) at chunk
+// j ^ (dim mod 16), each thread transposing an 8 keys x 8 dims block in registers.
 template <int D>
-__global__ __launch_bounds__(512) void attn_prefill_lds_kernel(const bf16* __restrict__ q,
-                                                               const bf16* __restrict__ kc,
-                                                               const bf16* __restrict__ vc,
-                                                               bf16* __restrict__ o, int S, int S_pad,
-                                                               int H, int S_max, int o_il) {
-  constexpr int NCH = D / 8;             // 16-byte chunks per key row
-  constexpr int RPB = 128 / D;           // key rows per 256 bytes
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kPfKV];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[kPfKV];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.x, b = bh / H, h = bh - b * H, d = H * D;
-  const size_t head = ((size_t)b * H + h) * S_max * D;
-  const int fr = lane & 15, fg = lane >> 4;
-
-  // K row `key`, chunk c at chunk c ^ ((key / RPB) mod NCH) of the row
-  for (int i = tid; i < S_pad * NCH; i += 512) {
+__device__ __forceinline__ void pf_stage(const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+                                         size_t head, int S, int kw0, int Wp, bf16* Ks, bf16* Vt, int tid) {
+  constexpr int NCH = D / 8, RPB = 128 / D;
+  for (int i = tid; i < Wp * NCH; i += 512) {
     const int key = i / NCH, c = i - key * NCH;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (key < S) v = *reinterpret_cast<const uint4*>(kc + head + (size_t)key * D + c * 8);
+    if (kw0 + key < S) v = *reinterpret_cast<const uint4*>(kc + head + (size_t)(kw0 + key) * D + c * 8);
     *reinterpret_cast<uint4*>(&Ks[key * D + ((c ^ ((key / RPB) & (NCH - 1))) << 3)]) = v;
   }
-  // V^T row `dim` (S_pad keys), chunk j (keys 8 j .. + 8) at chunk j ^ (dim mod 16); each
-  // thread transposes an 8 keys x 8 dims block in registers
-  for (int i = tid; i < (S_pad / 8) * NCH; i += 512) {
+  for (int i = tid; i < (Wp / 8) * NCH; i += 512) {
     const int kb = i / NCH, c = i - kb * NCH;
     uint32_t e[8][4];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int key = kb * 8 + r;
+      const int key = kw0 + kb * 8 + r;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (key < S) v = *reinterpret_cast<const uint4*>(vc + head + (size_t)key * D + c * 8);
       e[r][0] = v.x; e[r][1] = v.y; e[r][2] = v.z; e[r][3] = v.w;
@@ -492,95 +473,196 @@ __global__ __launch_bounds__(512) void attn_prefill_lds_kernel(const bf16* __res
       for (int pr = 0; pr < 4; ++pr)
         w4[pr] = ((e[2 * pr][wd] >> sh) & 0xffffu) | (((e[2 * pr + 1][wd] >> sh) & 0xffffu) << 16);
       const int dim = c * 8 + j;
-      *reinterpret_cast<uint4*>(&Vt[dim * S_pad + ((kb ^ (dim & 15)) << 3)]) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      *reinterpret_cast<uint4*>(&Vt[dim * Wp + ((kb ^ (dim & 15)) << 3)]) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
   }
-  __syncthreads();
+}
 
-  const int nqb = (S + 15) / 16;
-  for (int base = 0; base < nqb; base += 16) {
-    for (int half = 0; half < 2; ++half) {
-      const int qb = base + (half ? 15 - wv : wv);
-      if (qb >= nqb) continue;
-      const int q0 = qb * 16, qi = q0 + fr;          // this lane's query (all 4 lane groups)
-      const int nkt = (min(q0 + 16, S) + 15) / 16;  // key tiles up to the block's last query
-      // Q^T as the B operand: lane holds query qi, dims 32 c + 8 fg .. + 8
-      bf16x8 qb8[D / 32];
+// Running state of one 16-query block in one wave: O^T accumulators, oacc[t][r] =
+// O(query qi, dim 16 t + 4 fg + r) unnormalised, the running max and this lane's
+// share of the sum.
+template <int D>
+struct PfBlock {
+  f32x4 oacc[D / 16];
+  float m, lsum;
+};
+
+template <int D>
+__device__ __forceinline__ void pf_init(PfBlock<D>& s) {
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        qb8[c] = qi < S ? *reinterpret_cast<const bf16x8*>(q + ((size_t)b * S + qi) * d + h * D + c * 32 + fg * 8)
-                        : bf16x8{};
-      // O^T: oacc[t][r] = O(query qi, dim 16 t + 4 fg + r), unnormalised
-      f32x4 oacc[D / 16];
+  for (int t = 0; t < D / 16; ++t) s.oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  s.m = -INFINITY;
+  s.lsum = 0.f;
+}
+
+// Q^T as the B operand: lane holds query qi, dims 32 c + 8 fg .. + 8.
+template <int D>
+__device__ __forceinline__ void pf_load_q(const bf16* __restrict__ q, int b, int S, int d, int h, int qi,
+                                          int fg, bf16x8 (&qb8)[D / 32]) {
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float m = -INFINITY, lsum = 0.f;               // running max; this lane's share of the sum
-      for (int k0 = 0; k0 < nkt * 16; k0 += 32) {
-        // S^T for keys k0 .. k0 + 31: st[t2][r] = score(key k0 + 16 t2 + 4 fg + r, query qi)
-        f32x4 st[2];
+  for (int c = 0; c < D / 32; ++c)
+    qb8[c] = qi < S ? *reinterpret_cast<const bf16x8*>(q + ((size_t)b * S + qi) * d + h * D + c * 32 + fg * 8)
+                    : bf16x8{};
+}
+
+// Keys k_begin .. k_end - 1 (k_begin a multiple of 32, inside the window staged at
+// kw0 with Wp padded keys) for this lane's query qi.
+template <int D>
+__device__ __forceinline__ void pf_keys(PfBlock<D>& s, const bf16x8 (&qb8)[D / 32], const bf16* Ks,
+                                        const bf16* Vt, int kw0, int Wp, int k_begin, int k_end, int qi,
+                                        int S, int fr, int fg) {
+  constexpr int NCH = D / 8, RPB = 128 / D;
+  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
+    // S^T for keys k0 .. k0 + 31: st[t2][r] = score(key k0 + 16 t2 + 4 fg + r, query qi)
+    f32x4 st[2];
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          st[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const int key = k0 + t2 * 16 + fr;       // A-operand row of this lane
-          const int sw = (key / RPB) & (NCH - 1);
+    for (int t2 = 0; t2 < 2; ++t2) {
+      st[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = k0 - kw0 + t2 * 16 + fr;     // A-operand row of this lane (window-local)
+      const int sw = (key / RPB) & (NCH - 1);
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[key * D + (((c * 4 + fg) ^ sw) << 3)]);
-            st[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb8[c], st[t2], 0, 0, 0);
-          }
-        }
-        float cm = -INFINITY;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = k0 + t2 * 16 + fg * 4 + r;
-            if (key > qi || key >= S) st[t2][r] = -INFINITY;
-            cm = fmaxf(cm, st[t2][r]);
-          }
-        cm = max32(max16(cm));
-        const float mn = fmaxf(m, cm);
-        const float sc = m == -INFINITY ? 0.f : __expf(m - mn);
-        m = mn;
-        lsum *= sc;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) oacc[t] *= sc;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          bf16x4 ph, pl;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = st[t2][r] == -INFINITY ? 0.f : __expf(st[t2][r] - mn);
-            lsum += p;
-            const bf16 hi = f2bf(p);
-            ph[r] = bf_bits(hi);
-            pl[r] = bf_bits(f2bf(p - bf2f(hi)));
-          }
-          // V^T fragment: dim 16 t + fr, keys k0 + 16 t2 + 4 fg .. + 4 (half a swizzled chunk)
-          const int chunk = ((k0 + t2 * 16) >> 3) + (fg >> 1);
-#pragma unroll
-          for (int t = 0; t < D / 16; ++t) {
-            const int dim = t * 16 + fr;
-            const bf16x4 va = *reinterpret_cast<const bf16x4*>(&Vt[dim * S_pad + ((chunk ^ (dim & 15)) << 3) + ((fg & 1) << 2)]);
-            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, oacc[t], 0, 0, 0);
-            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, oacc[t], 0, 0, 0);
-          }
-        }
-      }
-      // the query's sum: the four lane groups' shares (the same value in every lane)
-      lsum = sum32(sum16(lsum));
-      if (qi < S) {
-        const float inv = 1.f / lsum;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const int dim = t * 16 + fg * 4;
-          uint2 u;
-          u.x = (uint32_t)f2bf(oacc[t][0] * inv) | ((uint32_t)f2bf(oacc[t][1] * inv) << 16);
-          u.y = (uint32_t)f2bf(oacc[t][2] * inv) | ((uint32_t)f2bf(oacc[t][3] * inv) << 16);
-          *reinterpret_cast<uint2*>(o + il_off(b * S + qi, h * D + dim, d, o_il)) = u;
-        }
+      for (int c = 0; c < D / 32; ++c) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[key * D + (((c * 4 + fg) ^ sw) << 3)]);
+        st[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb8[c], st[t2], 0, 0, 0);
       }
     }
+    float cm = -INFINITY;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + t2 * 16 + fg * 4 + r;
+        if (key > qi || key >= S) st[t2][r] = -INFINITY;
+        cm = fmaxf(cm, st[t2][r]);
+      }
+    cm = max32(max16(cm));
+    const float mn = fmaxf(s.m, cm);
+    const float sc = s.m == -INFINITY ? 0.f : __expf(s.m - mn);
+    s.m = mn;
+    s.lsum *= sc;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) s.oacc[t] *= sc;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      bf16x4 ph, pl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = st[t2][r] == -INFINITY ? 0.f : __expf(st[t2][r] - mn);
+        s.lsum += p;
+        const bf16 hi = f2bf(p);
+        ph[r] = bf_bits(hi);
+        pl[r] = bf_bits(f2bf(p - bf2f(hi)));
+      }
+      // V^T fragment: dim 16 t + fr, keys k0 + 16 t2 + 4 fg .. + 4 (half a swizzled chunk)
+      const int chunk = ((k0 - kw0 + t2 * 16) >> 3) + (fg >> 1);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const int dim = t * 16 + fr;
+        const bf16x4 va = *reinterpret_cast<const bf16x4*>(&Vt[dim * Wp + ((chunk ^ (dim & 15)) << 3) + ((fg & 1) << 2)]);
+        s.oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, s.oacc[t], 0, 0, 0);
+        s.oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, s.oacc[t], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Normalise and store this lane's query (8-byte stores in the output layout).
+template <int D>
+__device__ __forceinline__ void pf_store(PfBlock<D>& s, bf16* __restrict__ o, int b, int S, int d, int h,
+                                         int qi, int fg, int o_il) {
+  // the query's sum: the four lane groups' shares (the same value in every lane)
+  const float lsum = sum32(sum16(s.lsum));
+  if (qi >= S) return;
+  const float inv = 1.f / lsum;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const int dim = t * 16 + fg * 4;
+    uint2 u;
+    u.x = (uint32_t)f2bf(s.oacc[t][0] * inv) | ((uint32_t)f2bf(s.oacc[t][1] * inv) << 16);
+    u.y = (uint32_t)f2bf(s.oacc[t][2] * inv) | ((uint32_t)f2bf(s.oacc[t][3] * inv) << 16);
+    *reinterpret_cast<uint2*>(o + il_off(b * S + qi, h * D + dim, d, o_il)) = u;
+  }
+}
+
+// Prompt pass, bf16, K and V of one (sequence, head) in LDS.  One WG of 8 waves per
+// (sequence, head).  The head's keys go to LDS row-major and its values transposed
+// (64 KB each at most); then every wave works through 16-query blocks with no
+// further block barrier, taking blocks w and 15 - w of each 16 so the causal work is
+// even.  Scores are formed transposed, S^T = K Q^T, so each lane holds four
+// consecutive keys of one query: exactly the B operand of the 16 x 16 x 16 MFMA, which
+// then computes O^T = V^T P^T straight from registers.  Online softmax per 32 keys
+// (running max, per-lane partial sums merged at the end); P enters the product as
+// bf16 high and low parts (p = hi + lo to ~16 bits).  Both LDS arrays are XOR-swizzled
+// by 16-byte chunk so the 16 lanes that read 16 keys (or 16 value rows) at one offset
+// hit distinct banks.
+// A head longer than one window W = 32768 / D keys (S up to 2 W) is staged in two
+// windows: blocks whose queries lie in the first window finish there; the blocks of
+// the second window (W / 128 per wave) run over the first window's keys, keep their
+// state in registers across the restaging barrier, and finish over the second's.
+template <int D>
+__global__ __launch_bounds__(512) void attn_prefill_lds_kernel(const bf16* __restrict__ q,
+                                                               const bf16* __restrict__ kc,
+                                                               const bf16* __restrict__ vc,
+                                                               bf16* __restrict__ o, int S, int S_pad,
+                                                               int H, int S_max, int o_il) {
+  constexpr int W = pf_window(D), ND = W / 128;   // window; second-window blocks per wave
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kPfKV];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[kPfKV];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x, b = bh / H, h = bh - b * H, d = H * D;
+  const size_t head = ((size_t)b * H + h) * S_max * D;
+  const int fr = lane & 15, fg = lane >> 4;
+  const bool two = S > W;                       // then S_pad == W
+  const int nqb = (S + 15) / 16;
+  const int nqb0 = two ? W / 16 : nqb;          // blocks that finish in the first window
+
+  pf_stage<D>(kc, vc, head, S, 0, S_pad, Ks, Vt, tid);
+  __syncthreads();
+
+  for (int base = 0; base < nqb0; base += 16) {
+    for (int half = 0; half < 2; ++half) {
+      const int qb = base + (half ? 15 - wv : wv);
+      if (qb >= nqb0) continue;
+      const int q0 = qb * 16, qi = q0 + fr;          // this lane's query (all 4 lane groups)
+      const int k_end = (min(q0 + 16, S) + 15) / 16 * 16;
+      bf16x8 qb8[D / 32];
+      pf_load_q<D>(q, b, S, d, h, qi, fg, qb8);
+      PfBlock<D> s;
+      pf_init(s);
+      pf_keys<D>(s, qb8, Ks, Vt, 0, S_pad, 0, k_end, qi, S, fr, fg);
+      pf_store<D>(s, o, b, S, d, h, qi, fg, o_il);
+    }
+  }
+  if (!two) return;
+
+  // second-window blocks nqb0 + i, i = 16 j2 + wv and 16 j2 + 15 - wv
+  PfBlock<D> def[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+    const int i = 16 * (j >> 1) + ((j & 1) ? 15 - wv : wv);
+    const int qi = (nqb0 + i) * 16 + fr;
+    pf_init(def[j]);
+    if (nqb0 + i < nqb) {
+      bf16x8 qb8[D / 32];
+      pf_load_q<D>(q, b, S, d, h, qi, fg, qb8);
+      pf_keys<D>(def[j], qb8, Ks, Vt, 0, W, 0, W, qi, S, fr, fg);
+    }
+  }
+  __syncthreads();                              // every wave done with the first window
+  pf_stage<D>(kc, vc, head, S, W, W, Ks, Vt, tid);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+    const int i = 16 * (j >> 1) + ((j & 1) ? 15 - wv : wv);
+    if (nqb0 + i >= nqb) continue;
+    const int q0 = (nqb0 + i) * 16, qi = q0 + fr;
+    const int k_end = (min(q0 + 16, S) + 15) / 16 * 16;
+    bf16x8 qb8[D / 32];
+    pf_load_q<D>(q, b, S, d, h, qi, fg, qb8);
+    pf_keys<D>(def[j], qb8, Ks, Vt, W, W, W, k_end, qi, S, fr, fg);
+    pf_store<D>(def[j], o, b, S, d, h, qi, fg, o_il);
   }
 }
 

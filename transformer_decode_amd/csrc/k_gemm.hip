@@ -43,7 +43,7 @@ __device__ __forceinline__ void epi_store(const EpiArgs& e, int m, int n, int N,
     st((T*)e.out + il_off(m, n, N, e.o_il), v);
   } else {
     float bv = e.bias ? ld((const T*)e.bias + n) : 0.f;
-    e.out_f32[(size_t)m * N + n] = acc + bv;
+    e.out_f32[(size_t)m * (e.ldo ? e.ldo : N) + n] = acc + bv;
   }
 }
 
@@ -97,7 +97,7 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, int m, int n, int N
     *reinterpret_cast<float4*>(e.h + (size_t)m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
     st_bf4((bf16*)e.out + il_off(m, n, N, e.o_il), v);
   } else {
-    *reinterpret_cast<float4*>(e.out_f32 + (size_t)m * N + n) =
+    *reinterpret_cast<float4*>(e.out_f32 + (size_t)m * (e.ldo ? e.ldo : N) + n) =
         make_float4(acc[0] + b[0], acc[1] + b[1], acc[2] + b[2], acc[3] + b[3]);
   }
 }
@@ -143,7 +143,7 @@ __device__ __forceinline__ void epi_store8(const EpiArgs& e, int m, int n, int N
   } else {
 #pragma unroll
     for (int c = 0; c < 8; ++c) v[c] = acc[c] + b[c];
-    store8(e.out_f32 + (size_t)m * N + n, v);
+    store8(e.out_f32 + (size_t)m * (e.ldo ? e.ldo : N) + n, v);
   }
 }
 

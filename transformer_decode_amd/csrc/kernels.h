@@ -82,7 +82,8 @@ struct EpiArgs {
   // EPI_RELU (out = round(relu(acc + bias))) / EPI_POSADD
   void* out = nullptr;            // [M, N] storage type
   // EPI_F32
-  float* out_f32 = nullptr;       // [M, N]
+  float* out_f32 = nullptr;       // [M, N], rows ldo apart (ldo 0: N)
+  int ldo = 0;
   // layout of the bf16 weight W: 0 row-major, else the inference layout (il_off)
   int w_il = 0;
   // layout of the bf16 activations X (over K) and `out` (over N): 0 row-major, else the
