@@ -18,7 +18,14 @@ token under the actor.  The pages give no sampler.  Reading taken here:
   output word n mod 4; U = (top 24 bits of that word + 1/2) / 2^24, single precision
   as in the kernel;
 * the log-probability reported for a token t is logit_t / T' - logsumexp(logits / T')
-  with T' = T (T' = 1 for greedy), computed here in float64.
+  with T' = T (T' = 1 for greedy), computed here in float64;
+* top-p (nucleus) sampling with 0 < p < 1 (T > 0): the pick is restricted to the
+  nucleus, the smallest set of most probable tokens whose probability under
+  softmax(logits / T) reaches p (Holtzman et al., "The curious case of neural text
+  degeneration", ICLR 2020), with every token tied with the least probable member
+  included; Gumbel-max over the nucleus draws from the renormalised distribution.
+  The same uniforms are used, and the reported log-probability stays that of the
+  untruncated softmax(logits / T).
 """
 from __future__ import annotations
 
@@ -89,29 +96,61 @@ def logsumexp(x: np.ndarray, axis: int = -1) -> np.ndarray:
     return (m + np.log(np.sum(np.exp(x - m), axis=axis, keepdims=True))).squeeze(axis)
 
 
+def nucleus(scaled: np.ndarray, top_p: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Nucleus of each row of tempered logits [B, V] (float64) for 0 < top_p < 1.
+
+    Tokens sorted by probability, the nucleus is the first k of them whose cumulative
+    probability reaches top_p, plus every token tied with the k-th.  Returns (mask
+    [B, V], margin [B]): the margin is how far top_p is from the cumulative
+    probability of the first k - 1 and of the first k tokens, the room a rounding
+    change has before k moves.
+    """
+    scaled = np.asarray(scaled, dtype=np.float64)
+    prob = np.exp(scaled - logsumexp(scaled, axis=1)[:, None])
+    order = np.argsort(-prob, axis=1, kind="stable")
+    sp = np.take_along_axis(prob, order, axis=1)
+    cum = np.cumsum(sp, axis=1)
+    hit = cum >= top_p
+    # index of the k-th token (0-based); the whole row if rounding keeps the total below p
+    k = np.where(hit.any(axis=1), np.argmax(hit, axis=1), scaled.shape[1] - 1)
+    rows = np.arange(len(scaled))
+    kth = scaled[rows, order[rows, k]]
+    mask = scaled >= kth[:, None]
+    below = np.where(k > 0, cum[rows, np.maximum(k - 1, 0)], 0.0)
+    margin = np.minimum(top_p - below, cum[rows, k] - top_p)
+    return mask, margin
+
+
 def pick(logits: np.ndarray, temperature: float, seed: int, rows: np.ndarray,
-         position: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+         position: int, top_p: float = 1.0) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """One step for rows of logits [B, V] (float64).
 
     Returns (tokens [B], log-probabilities [B], decision margin [B]): the margin is the
     gap between the best and second-best of the quantity maximised (logits for greedy,
-    logit / T + G for sampling), the part of the decision a rounding change can flip.
+    logit / T + G for sampling, over the nucleus under top-p), the part of the decision
+    a rounding change can flip.  Under top-p it is the smaller of that gap and the
+    nucleus margin.
     """
     logits = np.asarray(logits, dtype=np.float64)
+    extra = np.full(len(logits), np.inf)
     if temperature > 0:
         scaled = logits / temperature
         y = scaled + gumbel(uniforms(seed, rows, position, logits.shape[1])).astype(np.float64)
+        if 0 < top_p < 1:
+            mask, extra = nucleus(scaled, top_p)
+            y = np.where(mask, y, -np.inf)
     else:
         scaled = logits
         y = logits
     tok = O.argmax_lowest(y)
     top2 = np.sort(y, axis=1)[:, -2:]
     lp = scaled[np.arange(len(tok)), tok] - logsumexp(scaled, axis=1)
-    return tok, lp, top2[:, 1] - top2[:, 0]
+    return tok, lp, np.minimum(top2[:, 1] - top2[:, 0], extra)
 
 
 def sampled_generate(model: O.OracleModel, prompts, gen_len: int, max_seq: int, temperature: float,
-                     seed: int, forced=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray, List[np.ndarray]]:
+                     seed: int, forced=None, top_p: float = 1.0
+                     ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, List[np.ndarray]]:
     """Generate gen_len tokens per row (the greedy loop of opt_he.greedy_generate with
     `pick` as the rule).  Token j of every row is generated at position S + j.
     Returns (tokens [B, gen_len], log-probabilities [B, gen_len], margins [B, gen_len],
@@ -124,10 +163,10 @@ def sampled_generate(model: O.OracleModel, prompts, gen_len: int, max_seq: int, 
     margins = np.zeros((B, gen_len))
     lg, cache = model.prefill(prompts, max_seq)
     logits = [lg]
-    toks[:, 0], lps[:, 0], margins[:, 0] = pick(lg, temperature, seed, rows, S)
+    toks[:, 0], lps[:, 0], margins[:, 0] = pick(lg, temperature, seed, rows, S, top_p)
     for j in range(1, gen_len):
         fed = toks[:, j - 1] if forced is None else np.asarray(forced)[:, j - 1]
         lg = model.decode(fed, cache)
         logits.append(lg)
-        toks[:, j], lps[:, j], margins[:, j] = pick(lg, temperature, seed, rows, S + j)
+        toks[:, j], lps[:, j], margins[:, j] = pick(lg, temperature, seed, rows, S + j, top_p)
     return toks, lps, margins, logits

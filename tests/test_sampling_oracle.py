@@ -112,3 +112,68 @@ def test_sampled_generation_is_reproducible_and_seed_dependent(T):
     c = SM.sampled_generate(om(), prompts, wl.gen_len, wl.max_seq, T, 43)[0]
     assert np.array_equal(a, b)
     assert not np.array_equal(a, c)
+
+
+# ------------------------------------------------------------------------------------
+# top-p (nucleus)
+# ------------------------------------------------------------------------------------
+
+def test_nucleus_is_the_smallest_set_reaching_p_brute_force():
+    """Over every subset of a 7-token vocabulary: the nucleus is the subset of fewest
+    tokens whose probability reaches p (the most probable one among those)."""
+    import itertools
+    rng = np.random.default_rng(21)
+    V = 7
+    for trial in range(60):
+        lg = rng.normal(size=(1, V)) * rng.uniform(0.3, 3.0)
+        p = rng.uniform(0.05, 0.98)
+        prob = scipy.special.softmax(lg[0])
+        best = None
+        for k in range(1, V + 1):
+            sets = [c for c in itertools.combinations(range(V), k) if prob[list(c)].sum() >= p]
+            if sets:
+                best = max(sets, key=lambda c: prob[list(c)].sum())
+                break
+        mask, margin = SM.nucleus(lg, p)
+        assert set(np.nonzero(mask[0])[0]) == set(best), (trial, p, prob)
+        assert margin[0] > 0
+
+
+def test_nucleus_includes_ties_and_limits():
+    lg = np.log(np.array([[0.4, 0.2, 0.2, 0.1, 0.1]]))
+    mask, margin = SM.nucleus(lg, 0.5)          # 0.4 + 0.2 reaches 0.5; the other 0.2 is tied
+    assert mask[0].tolist() == [True, True, True, False, False]
+    mask, _ = SM.nucleus(lg, 0.3)
+    assert mask[0].tolist() == [True, False, False, False, False]
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(6, 300))
+    # p -> 0 keeps only the most probable token: sampling becomes greedy
+    tok, _, _ = SM.pick(x, 0.9, 3, np.arange(6), 17, top_p=1e-9)
+    assert np.array_equal(tok, O.argmax_lowest(x))
+    # p = 1 is plain sampling, bit for bit
+    a = SM.pick(x, 0.9, 3, np.arange(6), 17, top_p=1.0)
+    b = SM.pick(x, 0.9, 3, np.arange(6), 17)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+    # the reported log-probability is that of the untruncated distribution
+    tok, lp, _ = SM.pick(x, 0.9, 3, np.arange(6), 17, top_p=0.3)
+    full = x / 0.9 - SM.logsumexp(x / 0.9, axis=1)[:, None]
+    np.testing.assert_allclose(lp, full[np.arange(6), tok], rtol=0, atol=1e-12)
+
+
+def test_top_p_draws_the_renormalised_nucleus():
+    """Chi-square over many positions: picks follow softmax(logits / T) restricted to
+    the nucleus and renormalised; nothing outside it is ever drawn."""
+    logits = np.array([[0.3, -1.2, 2.0, 0.0, 1.1, -0.4]])
+    T, p = 0.8, 0.7
+    prob = scipy.special.softmax(logits[0] / T)
+    mask, _ = SM.nucleus(logits / T, p)
+    want = np.where(mask[0], prob, 0.0)
+    want /= want.sum()
+    n = 30000
+    counts = np.zeros(logits.shape[1])
+    for pos in range(n):
+        tok, _, _ = SM.pick(logits, T, 9, np.array([1]), pos, top_p=p)
+        counts[tok[0]] += 1
+    assert counts[~mask[0]].sum() == 0
+    chi2 = scipy.stats.chisquare(counts[mask[0]], n * want[mask[0]])
+    assert chi2.pvalue > 1e-3, (counts / n, want)
