@@ -15,8 +15,9 @@ token under the actor.  The pages give no sampler.  Reading taken here:
 * U_n comes from the counter-based generator Philox4x64-10 (Salmon, Moraes, Dror,
   Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011): one block per four
   columns, counter (n div 4, row, position of the generated token, 0), key (seed, 0),
-  output word n mod 4; U = (top 24 bits of that word + 1/2) / 2^24, single precision
-  as in the kernel;
+  output word n mod 4; U = (top 23 bits of that word + 1/2) / 2^23, exact in single
+  precision (with 24 bits the float32 sum k + 1/2 rounds the largest k up to 2^24,
+  giving U = 1 and an infinite G), so U lies in [2^-24, 1 - 2^-24];
 * the log-probability reported for a token t is logit_t / T' - logsumexp(logits / T')
   with T' = T (T' = 1 for greedy), computed here in float64;
 * top-p (nucleus) sampling with 0 < p < 1 (T > 0): the pick is restricted to the
@@ -79,8 +80,13 @@ def uniforms(seed: int, rows: np.ndarray, position: int, V: int) -> np.ndarray:
            np.zeros((len(rows), nb), dtype=np.uint64))
     w = philox4x64_10(ctr, (np.uint64(seed), np.uint64(0)))       # [4, rows, nb]
     w = np.moveaxis(w, 0, -1).reshape(len(rows), 4 * nb)[:, :V]    # column n = word n % 4 of block n // 4
-    top = (w >> np.uint64(40)).astype(np.float32)
-    return (top + np.float32(0.5)) * np.float32(2.0 ** -24)
+    return word_uniform(w)
+
+
+def word_uniform(w) -> np.ndarray:
+    """U = (top 23 bits of the 64-bit word + 1/2) / 2^23 in float32 (exact)."""
+    top = (np.asarray(w, dtype=np.uint64) >> np.uint64(41)).astype(np.float32)
+    return (top + np.float32(0.5)) * np.float32(2.0 ** -23)
 
 
 def gumbel(u: np.ndarray) -> np.ndarray:
@@ -128,16 +134,15 @@ def pick(logits: np.ndarray, temperature: float, seed: int, rows: np.ndarray,
     Returns (tokens [B], log-probabilities [B], decision margin [B]): the margin is the
     gap between the best and second-best of the quantity maximised (logits for greedy,
     logit / T + G for sampling, over the nucleus under top-p), the part of the decision
-    a rounding change can flip.  Under top-p it is the smaller of that gap and the
-    nucleus margin.
+    a rounding change can flip.  The nucleus's own margin (in probability mass) is
+    the second value of ``nucleus``.
     """
     logits = np.asarray(logits, dtype=np.float64)
-    extra = np.full(len(logits), np.inf)
     if temperature > 0:
         scaled = logits / temperature
         y = scaled + gumbel(uniforms(seed, rows, position, logits.shape[1])).astype(np.float64)
         if 0 < top_p < 1:
-            mask, extra = nucleus(scaled, top_p)
+            mask, _ = nucleus(scaled, top_p)
             y = np.where(mask, y, -np.inf)
     else:
         scaled = logits
@@ -145,7 +150,7 @@ def pick(logits: np.ndarray, temperature: float, seed: int, rows: np.ndarray,
     tok = O.argmax_lowest(y)
     top2 = np.sort(y, axis=1)[:, -2:]
     lp = scaled[np.arange(len(tok)), tok] - logsumexp(scaled, axis=1)
-    return tok, lp, np.minimum(top2[:, 1] - top2[:, 0], extra)
+    return tok, lp, top2[:, 1] - top2[:, 0]
 
 
 def sampled_generate(model: O.OracleModel, prompts, gen_len: int, max_seq: int, temperature: float,

@@ -52,6 +52,18 @@ def test_uniforms_open_interval_and_moments():
     assert not np.array_equal(SM.uniforms(11, np.arange(2), 300, 64), SM.uniforms(12, np.arange(2), 300, 64))
 
 
+def test_uniform_extremes_stay_inside_the_interval():
+    """The smallest and largest words map to 2^-24 and 1 - 2^-24 exactly, so G is
+    finite for every word; neighbouring top values stay distinct."""
+    w = np.array([0, (1 << 41) - 1, 1 << 41, (1 << 64) - 1, ((1 << 64) - 1) ^ (1 << 41)], dtype=np.uint64)
+    u = SM.word_uniform(w)
+    assert u.dtype == np.float32
+    assert u[0] == np.float32(2.0 ** -24) and u[1] == u[0]
+    assert u[2] == np.float32(3 * 2.0 ** -24)
+    assert u[3] == np.float32(1 - 2.0 ** -24) and u[4] < u[3]
+    assert np.isfinite(SM.gumbel(u)).all()
+
+
 def test_logsumexp_matches_scipy():
     rng = np.random.default_rng(3)
     for scale in (0.1, 1.0, 30.0):
