@@ -426,6 +426,13 @@ def main():
             E[0].record(st)
             he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp, out.data_ptr(), lpb.data_ptr())
             E[1].record(st)
+            # the same with a top-p 0.9 nucleus (graph captured by the first call)
+            smp_p = he.he_sampling(0.7, 1234, 0.9)
+            Ep = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp_p, out.data_ptr(), lpb.data_ptr())
+            Ep[0].record(st)
+            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp_p, out.data_ptr(), lpb.data_ptr())
+            Ep[1].record(st)
             he.he_kernel_timer(ctx, he.HE_K_LMHEAD, True)
             he.he_generate_ex(ctx, prompts.data_ptr(), B, S, 8, smp, out.data_ptr(), lpb.data_ptr())
             lm_s = he.he_kernel_stats(ctx, he.HE_K_LMHEAD)
@@ -434,10 +441,12 @@ def main():
             he.he_sync(ctx)
             torch.cuda.synchronize()
         t_smp = E[0].elapsed_time(E[1]) / 1e3
+        t_topp = Ep[0].elapsed_time(Ep[1]) / 1e3
         lps = lpb.cpu().numpy()
         res["sampled"] = {
             "temperature": 0.7, "gen_ms": t_smp * 1e3, "gen_tokens_per_s": B * G / t_smp,
             "vs_greedy_gen": (t_pre + t_dec) / t_smp,
+            "top_p_0.9_gen_ms": t_topp * 1e3, "top_p_vs_greedy_gen": (t_pre + t_dec) / t_topp,
             "lmhead_us_sampled_logprobs": lm_s.total_ms / lm_s.launches * 1e3 if lm_s.launches else None,
             "lmhead_us_greedy": kern["lmhead"]["avg_us"] if "lmhead" in kern else None,
             "mean_logprob": float(lps.mean()), "logprobs_finite": bool((lps == lps).all())}

@@ -245,13 +245,20 @@ he_status he_generate(he_ctx* ctx, const int32_t* d_prompt, int32_t B, int32_t S
  * temperature == 0: greedy (largest logit, lowest index on ties).
  * temperature  > 0: the next token is drawn from softmax(logits / temperature) by
  *   the Gumbel-max rule: argmax_n (logit_n / temperature + G_n), G_n = -log(-log U_n),
- *   U_n = (top 24 bits of word n mod 4 of Philox4x64-10 (Salmon et al., SC 2011)
+ *   U_n = (top 23 bits of word n mod 4 of Philox4x64-10 (Salmon et al., SC 2011)
  *   at counter (n div 4, batch row, position of the token, 0), key (seed, 0) + 1/2)
- *   / 2^24.  A pick is a function of (seed, row, position, logits) only: the same
- *   seed reproduces a generation exactly. */
+ *   / 2^23, exact in float32 and strictly inside (0, 1).  A pick is a function of (seed, row, position, logits) only: the same
+ *   seed reproduces a generation exactly.
+ * top_p in (0, 1) with temperature > 0: nucleus sampling (Holtzman et al., ICLR
+ *   2020): the same rule restricted to the smallest set of most probable tokens
+ *   whose probability under softmax(logits / temperature) reaches top_p, every
+ *   token tied with its least probable member included; the threshold is found by
+ *   fixed-order sums, so picks stay reproducible.  0 or >= 1 turns it off; it needs
+ *   a vocabulary of at most 53248 tokens. */
 typedef struct he_sampling {
   float temperature;
   uint64_t seed;
+  float top_p;
 } he_sampling;
 
 /* he_generate with a pick rule and per-token log-probabilities.  smp == NULL is
@@ -260,10 +267,23 @@ typedef struct he_sampling {
  * with T' = temperature (1 for greedy), the row's logsumexp combined over vocabulary
  * blocks in a fixed order.  Device memory, caller-owned; written by the end of the
  * call's stream work.
+ * The log-probability is that of the untruncated distribution, also under top-p.
  * Errors as he_generate, plus HE_E_ARG for a temperature that is negative, not
- * finite, or so small that its reciprocal overflows. */
+ * finite, or so small that its reciprocal overflows, or a top_p that is negative
+ * or NaN; HE_E_UNSUPPORTED for top-p over a vocabulary above 53248. */
 he_status he_generate_ex(he_ctx* ctx, const int32_t* d_prompt, int32_t B, int32_t S_p,
                          int32_t S_g, const he_sampling* smp, int32_t* d_out, float* d_logprobs);
+
+/* The pick rule of he_generate_ex applied to caller logits: d_logits [B, vocab]
+ * float32 (device, row-major), row b drawn with batch row index b and token position
+ * `position` in the generator's counter, exactly as the generation step draws token
+ * `position` of row b.  d_tokens [B] int32 receives the picks; d_logprobs [B]
+ * float32 (may be NULL) their log-probabilities.  Uses the workspace's scratch but
+ * leaves the generation state alone.  Errors: HE_E_NOCACHE, HE_E_ARG (NULL buffer,
+ * batch outside 1..max_batch, negative position, bad rule as he_generate_ex),
+ * HE_E_UNSUPPORTED (not an LM-head model; top-p over a vocabulary above 53248). */
+he_status he_sample(he_ctx* ctx, const float* d_logits, int32_t B, int32_t position,
+                    const he_sampling* smp, int32_t* d_tokens, float* d_logprobs);
 
 /* Reward scoring (page 1, pipeline section: the reward model gives each response
  * a scalar score): full causal pass over d_ids [B, S] of a HE_HEAD_SCALAR model,

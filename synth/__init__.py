@@ -152,6 +152,17 @@ def tokens(seed: int, name: str, shape, vocab: int) -> torch.Tensor:
     return torch.from_numpy(g.integers(0, vocab, size=shape, dtype=np.int64).astype(np.int32))
 
 
+def sample_logits(B: int, V: int, seed: int = 0, spread: float = 2.0, head: float = 1.1) -> torch.Tensor:
+    """[B, V] float32 logits shaped like a language model's: N(0, spread) noise on a
+    Zipf-like profile -head * log(1 + rank) over a seeded permutation of the columns
+    (a few likely tokens, a long tail)."""
+    g = _stream(seed, "logit_ranks", 0)
+    rank = g.permutation(V).astype(np.float32)
+    base = (-np.float32(head) * np.log1p(rank)).astype(np.float32)
+    x = normal(seed, "logits", (B, V), std=spread, dtype=torch.float32).numpy()
+    return torch.from_numpy((x + base[None, :]).astype(np.float32))
+
+
 def _threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))

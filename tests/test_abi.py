@@ -30,8 +30,8 @@ def _declared():
 def test_exports_every_declared_call():
     names = _declared()
     assert "he_generate" in names and "he_generate_ex" in names and "he_fuse_lora" in names
-    assert "he_logprobs" in names
-    assert len(names) >= 19
+    assert "he_logprobs" in names and "he_sample" in names
+    assert len(names) >= 20
     L = ctypes.CDLL(he.LIB_PATH)
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
@@ -122,6 +122,18 @@ def test_state_machine_generation_cycle():
     e.close()
 
 
+def test_top_p_vocabulary_limit():
+    """The nucleus kernel holds a row of at most 53248 logits in registers."""
+    import dataclasses
+    shape = dataclasses.replace(synth.WORKLOADS["opt125m"].actor, n_layers=1, vocab=53264)
+    e = he.Engine(shape, _fake_params(shape), validate_only=True)
+    ctx, P = e.ctx, 0x1234
+    he.he_retake_cache(ctx, 2, 32)
+    assert _status(he.he_generate_ex, ctx, P, 2, 16, 8, he.he_sampling(0.7, 1, 0.9), P, P) == he.HE_E_UNSUPPORTED
+    he.he_generate_ex(ctx, P, 2, 16, 8, he.he_sampling(0.7, 1, 1.0), P, P)     # top-p off: fine
+    e.close()
+
+
 def test_unsupported_bf16_decode_shapes():
     """bf16 generation models need d and d_ffn divisible by 128 and vocab by 16."""
     import dataclasses
@@ -153,6 +165,18 @@ def test_argument_checks():
     he.he_generate_ex(ctx, P, 2, 16, 8, he.he_sampling(0.7, 123), P, 0)
     assert _status(he.he_generate_ex, ctx, P, 2, 16, 18, he.he_sampling(1.0, 1), P, P) == he.HE_E_RANGE
     assert _status(he.he_generate_ex, ctx, 0, 2, 16, 8, he.he_sampling(1.0, 1), P, P) == he.HE_E_ARG
+    # top-p: negative or NaN rejected; 0 and >= 1 mean off
+    for tp in (-0.1, float("nan")):
+        assert _status(he.he_generate_ex, ctx, P, 2, 16, 8, he.he_sampling(0.7, 1, tp), P, P) == he.HE_E_ARG
+    for tp in (0.0, 0.9, 1.0, 5.0):
+        he.he_generate_ex(ctx, P, 2, 16, 8, he.he_sampling(0.7, 1, tp), P, P)
+    # sampling caller logits
+    he.he_sample(ctx, P, 2, 0, None, P, 0)
+    he.he_sample(ctx, P, 1, 31, he.he_sampling(0.8, 3, 0.5), P, P)
+    for args, st in (((0, 2, 5, None, P, 0), he.HE_E_ARG), ((P, 2, 5, None, 0, 0), he.HE_E_ARG),
+                     ((P, 3, 5, None, P, 0), he.HE_E_ARG), ((P, 2, -1, None, P, 0), he.HE_E_ARG),
+                     ((P, 2, 5, he.he_sampling(-1.0, 0), P, 0), he.HE_E_ARG)):
+        assert _status(he.he_sample, ctx, *args) == st, args
     # teacher-forced scoring: 1 <= S_p < S <= max_seq, buffers non-NULL
     he.he_logprobs(ctx, P, 2, 32, 16, P)
     he.he_logprobs(ctx, P, 1, 2, 1, P)
@@ -219,5 +243,6 @@ def test_reward_model_only_scores():
     he.he_score(ctx, P, 128, 512, P)
     assert _status(he.he_prefill, ctx, P, 2, 16, P) == he.HE_E_UNSUPPORTED
     assert _status(he.he_logprobs, ctx, P, 2, 16, 8, P) == he.HE_E_UNSUPPORTED
+    assert _status(he.he_sample, ctx, P, 2, 0, None, P, 0) == he.HE_E_UNSUPPORTED
     assert _status(he.he_score, ctx, P, 129, 512, P) == he.HE_E_ARG
     e.close()

@@ -8,6 +8,8 @@ logits in the sampled decision); a row must agree on at least its first pick unl
 that one is already a near-tie.  Log-probabilities: at every compared position.  A
 log-probability is one logit minus a logsumexp, so its error is bounded by twice the
 workload's logit error bound: 2e-3 * max|logit| for the fp32 workload, 6e-2 for bf16."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -24,7 +26,7 @@ pytestmark = pytest.mark.gpu
 MARGIN = 1e-2
 
 
-def _run(wl, params, lora, prompts, gen_len, T, seed, use_graph=True, want_lp=True):
+def _run(wl, params, lora, prompts, gen_len, T, seed, use_graph=True, want_lp=True, top_p=0.0):
     run = GpuRun(wl, params, use_graph=use_graph)
     lt = run.lora(lora)
     B, S = prompts.shape
@@ -32,7 +34,7 @@ def _run(wl, params, lora, prompts, gen_len, T, seed, use_graph=True, want_lp=Tr
     out = torch.empty(B, gen_len, dtype=torch.int32, device="cuda")
     lp = torch.full((B, gen_len), float("nan"), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    smp = he.he_sampling(T, seed) if T is not None else None
+    smp = he.he_sampling(T, seed, top_p) if T is not None else None
     with torch.cuda.stream(run.stream):
         he.he_fuse_lora(run.ctx, lt)
         he.he_retake_cache(run.ctx, wl.batch, wl.max_seq)
@@ -131,4 +133,124 @@ def test_opt125m_sampling_reproducible_graph_and_seed(c2):
     # the greedy entry point is the temperature-0 rule without log-probabilities
     g_tok, _ = _run(C2, params, lora, prompts, G, None, 0, want_lp=False)
     z_tok, _ = _run(C2, params, lora, prompts, G, 0.0, 5)
+    assert np.array_equal(g_tok, z_tok)
+
+
+# ------------------------------------------------------------------------------------
+# the pick rule on caller logits (he_sample): both sides see the same float32 logits,
+# at the 6.7B workload's batch and vocabulary
+# ------------------------------------------------------------------------------------
+# The GPU forms s = logit * (1/T) and G in float32 and the nucleus masses as fp32 sums
+# of 52 terms per thread plus a 1024-way tree (relative error ~4e-6); the oracle works
+# in float64 on the same logits with float32 G.  Decisions are compared where they
+# survive those errors with room: a Gumbel-max gap above GAP_TOL, and the same pick
+# under nucleus masses p - MASS_TOL and p + MASS_TOL.
+GAP_TOL = 1e-4
+MASS_TOL = 1e-4
+LP_TOL = 1e-4
+
+
+def _robust(logits64, T, seed, rows, pos, P):
+    tok, lp, gap = SM.pick(logits64, T, seed, rows, pos, top_p=P)
+    ok = gap > GAP_TOL
+    if T > 0 and 0 < P < 1:
+        lo, _, _ = SM.pick(logits64, T, seed, rows, pos, top_p=max(P - MASS_TOL, 1e-9))
+        hi, _, _ = SM.pick(logits64, T, seed, rows, pos, top_p=min(P + MASS_TOL, 1.0))
+        ok &= (lo == tok) & (hi == tok)
+    return tok, lp, ok
+
+
+@pytest.fixture(scope="module")
+def head_only():
+    """The 6.7B workload's shape with no layers: only the head's tables exist."""
+    wl = synth.WORKLOADS["opt6.7b"]
+    shape = dataclasses.replace(wl.actor, n_layers=0)
+    return dataclasses.replace(wl, actor=shape), synth.model_params(shape)
+
+
+@pytest.mark.parametrize("T,P,pos", [(0.0, 1.0, 0), (0.7, 1.0, 300), (1.0, 0.9, 511), (0.7, 0.5, 7),
+                                     (1.3, 0.95, 256)])
+def test_sample_matches_oracle_on_given_logits(head_only, T, P, pos):
+    wl, params = head_only
+    B, V = wl.batch, wl.actor.vocab
+    x = synth.sample_logits(B, V, seed=pos + 1)
+    seed = 4242
+    run = GpuRun(wl, params)
+    d_x = x.cuda()
+    tok = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    lp = torch.full((B,), float("nan"), dtype=torch.float32, device="cuda")
+    smp = he.he_sampling(T, seed, P) if T > 0 else None
+    torch.cuda.synchronize()
+    with torch.cuda.stream(run.stream):
+        he.he_retake_cache(run.ctx, B, 16)
+        he.he_sample(run.ctx, d_x.data_ptr(), B, pos, smp, tok.data_ptr(), lp.data_ptr())
+        he.he_sync(run.ctx)
+    got_t, got_lp = tok.cpu().numpy(), lp.cpu().numpy()
+    run.close()
+    want_t, want_lp, ok = _robust(x.numpy().astype(np.float64), T, seed, np.arange(B), pos, P)
+    log(f"he_sample T={T} p={P} pos={pos}: {ok.sum()}/{B} rows decided with room")
+    assert ok.mean() >= 0.9
+    assert np.array_equal(got_t[ok], want_t[ok]), (got_t[ok], want_t[ok])
+    tol = LP_TOL * np.maximum(1.0, np.abs(want_lp))
+    assert (np.abs(got_lp.astype(np.float64) - want_lp) <= tol).all(), np.abs(got_lp - want_lp).max()
+    if T > 0 and 0 < P < 1:   # every pick lies in the nucleus (with the mass tolerance)
+        mask, _ = SM.nucleus(x.numpy().astype(np.float64) / T, min(P + MASS_TOL, 1.0))
+        assert mask[np.arange(B), got_t].all()
+
+
+# ------------------------------------------------------------------------------------
+# top-p generation: the decode loop applies exactly the rule he_sample applies
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [0.9, 0.5])
+def test_opt125m_top_p_generation_follows_the_rule_each_step(c2, P):
+    """Generate with top-p, then replay the same sequence: prefill and feed each
+    generated token (teacher forcing) to get every step's logits, and apply
+    he_sample with the same rule at the same position.  The generation's own picks
+    and log-probabilities must come back bit for bit: the loop's position counter,
+    its logits and its pick are those of the rule."""
+    params, lora, prompts_cpu = c2
+    B, S, T, seed, G = C2.batch, C2.prompt_len, 0.8, 606, 12
+    run = GpuRun(C2, params)
+    lt = run.lora(lora)
+    prompts = prompts_cpu.cuda()
+    smp = he.he_sampling(T, seed, P)
+    toks = torch.empty(B, G, dtype=torch.int32, device="cuda")
+    lps = torch.empty(B, G, dtype=torch.float32, device="cuda")
+    lg = torch.empty(B, C2.actor.vocab, dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    rt = torch.empty(B, dtype=torch.int32, device="cuda")
+    rl = torch.empty(B, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    replay_t, replay_l = [], []
+    with torch.cuda.stream(run.stream):
+        he.he_fuse_lora(run.ctx, lt)
+        he.he_retake_cache(run.ctx, B, C2.max_seq)
+        he.he_generate_ex(run.ctx, prompts.data_ptr(), B, S, G, smp, toks.data_ptr(), lps.data_ptr())
+        he.he_prefill(run.ctx, prompts.data_ptr(), B, S, nxt.data_ptr(), lg.data_ptr())
+        for j in range(G):
+            if j:
+                col = toks[:, j - 1].contiguous()
+                he.he_decode_step(run.ctx, col.data_ptr(), nxt.data_ptr(), lg.data_ptr())
+            he.he_sample(run.ctx, lg.data_ptr(), B, S + j, smp, rt.data_ptr(), rl.data_ptr())
+            he.he_sync(run.ctx)
+            replay_t.append(rt.cpu().numpy().copy())
+            replay_l.append(rl.cpu().numpy().copy())
+    a_t, a_l = toks.cpu().numpy(), lps.cpu().numpy()
+    run.close()
+    b_t, b_l = np.stack(replay_t, axis=1), np.stack(replay_l, axis=1)
+    assert np.array_equal(a_t, b_t)
+    assert np.array_equal(a_l.view(np.uint32), b_l.view(np.uint32))
+    # and the rule is not greedy: some picks differ from the argmax
+    assert len(set(a_t[:, 0].tolist())) > 1
+
+
+def test_opt125m_top_p_reproducible_and_limits(c2):
+    params, lora, prompts_cpu = c2
+    a_tok, a_lp = _run(C2, params, lora, prompts_cpu, G, 0.9, 77, top_p=0.8)
+    b_tok, b_lp = _run(C2, params, lora, prompts_cpu, G, 0.9, 77, use_graph=False, top_p=0.8)
+    assert np.array_equal(a_tok, b_tok) and np.array_equal(a_lp.view(np.uint32), b_lp.view(np.uint32))
+    # a vanishing nucleus keeps only the most probable token: greedy
+    g_tok, _ = _run(C2, params, lora, prompts_cpu, G, None, 0, want_lp=False)
+    z_tok, _ = _run(C2, params, lora, prompts_cpu, G, 0.9, 77, top_p=1e-6)
     assert np.array_equal(g_tok, z_tok)

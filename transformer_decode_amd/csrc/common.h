@@ -131,13 +131,14 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
 // Gumbel noise G = -log(-log U) of vocabulary columns 4 n4 .. 4 n4 + 3 for batch row
 // `row` generating the token at `position`: one generator block at counter
 // (n4, row, position, 0), key (seed, 0); column 4 n4 + w takes word w, and
-// U = (its top 24 bits + 1/2) / 2^24.
+// U = (its top 23 bits + 1/2) / 2^23, exact in float32 and inside [2^-24, 1 - 2^-24]
+// (24 bits would round the largest value up to U = 1, an infinite G).
 __device__ __forceinline__ void gumbel4(uint64_t seed, int row, int position, int n4, float g[4]) {
   uint64_t c[4] = {(uint64_t)n4, (uint64_t)row, (uint64_t)position, 0ull};
   philox4x64_10(c, seed, 0ull);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const float u = ((float)(uint32_t)(c[w] >> 40) + 0.5f) * 0x1p-24f;
+    const float u = ((float)(uint32_t)(c[w] >> 41) + 0.5f) * 0x1p-23f;
     g[w] = -logf(-logf(u));
   }
 }

@@ -82,6 +82,7 @@ struct he_ctx {
   int32_t* tokens = nullptr;
   int32_t* pos_dev = nullptr;     // position of the token the next step feeds
   int32_t* pos_next = nullptr;    // position of the token being picked (LM head -> finalize)
+  int32_t* spos = nullptr;        // [2] he_sample's own position pair (pos_dev, pos_next roles)
   float* logp = nullptr;          // [B_max][S_max + 1] log-probabilities of the picks
   float* best_lg = nullptr;       // per (row, LM-head column block): pick's tempered logit,
   float* blk_max = nullptr;       // the block's largest tempered logit and its sum of
@@ -94,6 +95,7 @@ struct he_ctx {
   float inv_temp = 0.f;
   uint64_t seed = 0;
   bool want_logp = false;
+  float top_p = 1.f;              // nucleus mass; >= 1 off
   // decode GEMM plans and activation row tiles for the current batch (set by the
   // prompt pass)
   GemvPlan p_qkv, p_out, p_fc1, p_fc2, p_lm;
@@ -111,6 +113,7 @@ struct he_ctx {
   float graph_itemp = 0.f;        // pick rule the graphs were captured with
   uint64_t graph_seed = 0;
   bool graph_logp = false;
+  float graph_topp = 1.f;
   bool capturing = false;
 
   Timer timers[HE_K_COUNT];
@@ -272,6 +275,8 @@ static void decode_partials(he_ctx* c, const void* X, const void* W, int B, int 
 // log-probability when asked); advances the position counter.
 static void enqueue_lm_head(he_ctx* c, int B, bool want_logits) {
   const int d = c->d, dt = c->dt;
+  const bool nucleus = c->top_p < 1.f;
+  want_logits = want_logits || nucleus;   // the nucleus needs the whole row
   const size_t es = esize(dt);
   hipStream_t st = c->stream;
   SampleArgs smp;
@@ -298,8 +303,12 @@ static void enqueue_lm_head(he_ctx* c, int B, bool want_logits) {
     run_k(c, HE_K_LMHEAD, (double)c->V * d * es, 2.0 * B * c->V * d,
           [&] { launch_gemv(dt, c->x, c->wt.tok_emb, B, c->V, d, c->p_lm, g, st); });
   }
-  launch_argmax_finalize(c->best_val, c->best_idx, smp, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
-                         c->want_logp ? c->logp : nullptr, c->max_seq + 1, c->pos_next, c->pos_dev, nullptr, st);
+  if (nucleus)
+    launch_topp_finalize(c->logits, B, c->V, smp, c->top_p, c->ids_cur, c->tokens, c->want_logp ? c->logp : nullptr,
+                         c->max_seq + 1, c->pos_next, c->pos_dev, st);
+  else
+    launch_argmax_finalize(c->best_val, c->best_idx, smp, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
+                           c->want_logp ? c->logp : nullptr, c->max_seq + 1, c->pos_next, c->pos_dev, nullptr, st);
 }
 
 // Decoder layers of the prompt pass of a pre-LN LM-head model over ids [B, S]: leaves
@@ -715,6 +724,7 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   const size_t o_a = take(rows * c->F * es);
   int argmax_cap = 0;
   const size_t part_elems = parts_elems(c, max_batch, &argmax_cap);
+  argmax_cap = std::max(argmax_cap, (c->V + 127) / 128);   // he_sample's 128-column blocks
   const size_t o_parts = take(part_elems * 4);
   const size_t o_logits = take((size_t)bpad * c->V * 4);
   const size_t o_bv = take((size_t)bpad * argmax_cap * 4);
@@ -727,6 +737,7 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   const size_t o_bsm = take((size_t)bpad * argmax_cap * 4);
   const size_t o_pos = take(256);
   const size_t o_posn = take(256);
+  const size_t o_spos = take(256);
   // one chunk of scoring-pass logits: up to kLogitChunk rows of the vocabulary
   const int lg_rows = c->desc.head == HE_HEAD_LM ? (int)std::min<size_t>(rows, kLogitChunk) : 0;
   const size_t o_lgc = take((size_t)lg_rows * c->V * 4);
@@ -770,6 +781,7 @@ he_status he_retake_cache(he_ctx* c, int32_t max_batch, int32_t max_seq) {
   c->tokens = (int32_t*)(scratch + o_tok);
   c->pos_dev = (int32_t*)(scratch + o_pos);
   c->pos_next = (int32_t*)(scratch + o_posn);
+  c->spos = (int32_t*)(scratch + o_spos);
   c->logp = (float*)(scratch + o_logp);
   c->best_lg = (float*)(scratch + o_blg);
   c->blk_max = (float*)(scratch + o_bmx);
@@ -822,6 +834,7 @@ static void set_greedy(he_ctx* c) {
   c->inv_temp = 0.f;
   c->seed = 0;
   c->want_logp = false;
+  c->top_p = 1.f;
 }
 
 he_status he_prefill(he_ctx* c, const int32_t* ids, int32_t B, int32_t S, int32_t* d_next, float* d_logits) {
@@ -853,7 +866,7 @@ static he_status run_step(he_ctx* c, bool want_logits) {
   if (graph) {
     hipGraphExec_t& ge = c->graph[want_logits ? 1 : 0];
     if (c->graph_B != B || c->graph_fused != c->fused || c->graph_itemp != c->inv_temp ||
-        c->graph_seed != c->seed || c->graph_logp != c->want_logp)
+        c->graph_seed != c->seed || c->graph_logp != c->want_logp || c->graph_topp != c->top_p)
       drop_graphs(c);
     if (!ge) {
       hipGraph_t g = nullptr;
@@ -871,6 +884,7 @@ static he_status run_step(he_ctx* c, bool want_logits) {
       c->graph_itemp = c->inv_temp;
       c->graph_seed = c->seed;
       c->graph_logp = c->want_logp;
+      c->graph_topp = c->top_p;
     }
     HIP_TRY(c, hipGraphLaunch(ge, c->stream));
   } else {
@@ -946,18 +960,71 @@ he_status he_generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, 
   return generate(c, d_prompt, B, S, S_g, d_out, nullptr);
 }
 
-he_status he_generate_ex(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g,
-                         const he_sampling* smp, int32_t* d_out, float* d_logprobs) {
-  if (!c) return HE_E_ARG;
+// Pick rule from he_sampling (NULL: greedy) into the context; checked before use.
+static he_status set_rule(he_ctx* c, const he_sampling* smp, bool want_logp) {
   const float t = smp ? smp->temperature : 0.f;
   if (!(t >= 0.f) || !std::isfinite(t))
     return set_err(c, HE_E_ARG, "temperature %g is not a finite value >= 0", (double)t);
   const float it = t > 0.f ? 1.f / t : 0.f;
   if (t > 0.f && !std::isfinite(it)) return set_err(c, HE_E_ARG, "temperature %g too small", (double)t);
+  const float tp = smp ? smp->top_p : 0.f;
+  if (!(tp >= 0.f)) return set_err(c, HE_E_ARG, "top_p %g is negative or NaN", (double)tp);
+  const bool nucleus = t > 0.f && tp > 0.f && tp < 1.f;
+  if (nucleus && c->V > topp_max_vocab())
+    return set_err(c, HE_E_UNSUPPORTED, "top-p over a vocabulary of %d (at most %d)", c->V, topp_max_vocab());
   c->inv_temp = it;
   c->seed = smp && t > 0.f ? smp->seed : 0;
-  c->want_logp = d_logprobs != nullptr;
+  c->want_logp = want_logp;
+  c->top_p = nucleus ? tp : 1.f;
+  return HE_OK;
+}
+
+he_status he_generate_ex(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g,
+                         const he_sampling* smp, int32_t* d_out, float* d_logprobs) {
+  if (!c) return HE_E_ARG;
+  he_status s = set_rule(c, smp, d_logprobs != nullptr);
+  if (s != HE_OK) return s;
   return generate(c, d_prompt, B, S, S_g, d_out, d_logprobs);
+}
+
+he_status he_sample(he_ctx* c, const float* d_logits, int32_t B, int32_t position, const he_sampling* smp,
+                    int32_t* d_tokens, float* d_logprobs) {
+  if (!c) return HE_E_ARG;
+  he_status s = check_compute(c);
+  if (s != HE_OK) return s;
+  if (c->desc.head != HE_HEAD_LM) return set_err(c, HE_E_UNSUPPORTED, "sampling needs an LM-head model");
+  if (!d_logits || !d_tokens) return set_err(c, HE_E_ARG, "NULL buffer");
+  if (B < 1 || B > c->max_batch) return set_err(c, HE_E_ARG, "batch %d outside 1..%d", B, c->max_batch);
+  if (position < 0) return set_err(c, HE_E_ARG, "position %d < 0", position);
+  // the rule of this call only: the context's own (used by he_decode_step) is kept
+  const float keep_it = c->inv_temp, keep_tp = c->top_p;
+  const uint64_t keep_seed = c->seed;
+  const bool keep_lp = c->want_logp;
+  s = set_rule(c, smp, d_logprobs != nullptr);
+  const float it = c->inv_temp, tp = c->top_p;
+  const uint64_t seed = c->seed;
+  const bool want_lp = c->want_logp;
+  c->inv_temp = keep_it; c->top_p = keep_tp; c->seed = keep_seed; c->want_logp = keep_lp;
+  if (s != HE_OK) return s;
+  if (c->validate_only) return HE_OK;
+  hipStream_t st = c->stream;
+  SampleArgs smpa;
+  smpa.inv_temp = it;
+  smpa.seed = seed;
+  if (want_lp) { smpa.best_lg = c->best_lg; smpa.blk_max = c->blk_max; smpa.blk_sum = c->blk_sum; }
+  launch_set_i32(c->spos, position - 1, st);
+  if (tp < 1.f) {
+    launch_set_i32(c->spos + 1, position, st);
+    launch_topp_finalize(d_logits, B, c->V, smpa, tp, nullptr, d_tokens, d_logprobs, 0, c->spos + 1,
+                         nullptr, st);
+  } else {
+    const int nb = (c->V + 127) / 128;
+    launch_reduce_argmax(d_logits, 1, B, c->V, nullptr, c->best_val, c->best_idx, nb, c->spos, c->spos + 1,
+                         smpa, st);
+    launch_argmax_finalize(c->best_val, c->best_idx, smpa, nb, B, nullptr, d_tokens,
+                           want_lp ? d_logprobs : nullptr, 0, c->spos + 1, nullptr, nullptr, st);
+  }
+  return check_launch(c, "sample launch");
 }
 
 // Teacher-forced scoring: prompt pass over the whole sequence, final LayerNorm of the

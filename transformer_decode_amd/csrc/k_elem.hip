@@ -505,10 +505,11 @@ __global__ __launch_bounds__(64) void argmax_finalize_kernel(
   }
   if (l == 0) {
     const int p = *pos_next;
+    const size_t oi = tok_stride ? (size_t)m * tok_stride + p : (size_t)m;
     if (bi == 0x7fffffff) bi = 0;
     if (ids_cur) ids_cur[m] = bi;
-    if (tokens) tokens[(size_t)m * tok_stride + p] = bi;
-    if (lse) logp[(size_t)m * tok_stride + p] = bl - (mx + logf(sum));
+    if (tokens) tokens[oi] = bi;
+    if (lse) logp[oi] = bl - (mx + logf(sum));
     if (d_next) d_next[m] = bi;
     if (m == 0 && pos_dev) *pos_dev = p;
   }
@@ -520,6 +521,129 @@ void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, cons
                             hipStream_t st) {
   argmax_finalize_kernel<<<M, 64, 0, st>>>(best_val, best_idx, smp, n_blocks, ids_cur, tokens, logp,
                                            tok_stride, pos_next, pos_dev, d_next);
+}
+
+// ---------------------------------------------------------------------------------
+// Top-p (nucleus) pick (Holtzman et al., ICLR 2020) from a row of fp32 logits, one
+// block of 1024 threads per row.  s = logit * inv_temp and e = exp(s - max) stay in
+// registers (kToppGroups groups of 4 columns per thread).  The nucleus threshold is
+// the largest order key c (an order-preserving map of s to 32 bits) whose mass
+// sum(e : key >= c) still reaches top_p * sum(e): found bit by bit from the top, each
+// test one fixed-order block sum, so the decision is the same on every run.  The pick
+// is the Gumbel-max rule over {key >= c} with the same Philox uniforms as the LM
+// head's epilogue; the log-probability is that of the untruncated softmax(s).
+// ---------------------------------------------------------------------------------
+constexpr int kToppThreads = 1024, kToppGroups = 13;
+
+__device__ __forceinline__ uint32_t ord_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+__global__ __launch_bounds__(kToppThreads) void topp_finalize_kernel(
+    const float* __restrict__ logits, int V, SampleArgs smp, float top_p, int32_t* __restrict__ ids_cur,
+    int32_t* __restrict__ tokens, float* __restrict__ logp, int tok_stride,
+    const int32_t* __restrict__ pos_next, int32_t* __restrict__ pos_dev) {
+  __shared__ float red[64];
+  __shared__ float bvs[kToppThreads / kWave];
+  __shared__ int bis[kToppThreads / kWave];
+  const int m = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int p = *pos_next;
+  const float* L = logits + (size_t)m * V;
+  const int ng = (V + 3) >> 2;
+  float sv[kToppGroups][4], ev[kToppGroups][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < kToppGroups; ++g) {
+    const int gi = tid + g * nt;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int col = 4 * gi + w;
+      sv[g][w] = (gi < ng && col < V) ? L[col] * smp.inv_temp : -INFINITY;
+      mx = fmaxf(mx, sv[g][w]);
+    }
+  }
+  mx = block_max(mx, red);
+  float z = 0.f;
+#pragma unroll
+  for (int g = 0; g < kToppGroups; ++g)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      ev[g][w] = sv[g][w] == -INFINITY ? 0.f : expf(sv[g][w] - mx);
+      z += ev[g][w];
+    }
+  const float Z = block_sum(z, red);
+  const float need = top_p * Z;
+  uint32_t c = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = c | (1u << bit);
+    float part = 0.f;
+#pragma unroll
+    for (int g = 0; g < kToppGroups; ++g)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (sv[g][w] != -INFINITY && ord_key(sv[g][w]) >= cand) part += ev[g][w];
+    if (block_sum(part, red + 32) >= need) c = cand;   // the same value in every thread
+  }
+  // the pick re-reads the row (from L2) rather than index the register copy by a
+  // loop counter the compiler keeps rolled
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll 1
+  for (int gi = tid; gi < ng; gi += nt) {
+    float gu[4];
+    gumbel4(smp.seed, m, p, gi, gu);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int col = 4 * gi + w;
+      if (col < V) {
+        const float sw = L[col] * smp.inv_temp;
+        if (ord_key(sw) >= c) {
+          const float y = sw + gu[w];
+          if (better(y, col, bv, bi)) { bv = y; bi = col; }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if ((tid & (kWave - 1)) == 0) { bvs[tid / kWave] = bv; bis[tid / kWave] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int i = 1; i < nt / kWave; ++i)
+      if (better(bvs[i], bis[i], bv, bi)) { bv = bvs[i]; bi = bis[i]; }
+    const size_t oi = tok_stride ? (size_t)m * tok_stride + p : (size_t)m;
+    if (bi == 0x7fffffff) bi = 0;
+    if (ids_cur) ids_cur[m] = bi;
+    if (tokens) tokens[oi] = bi;
+    if (logp) logp[oi] = L[bi] * smp.inv_temp - (mx + logf(Z));
+    if (m == 0 && pos_dev) *pos_dev = p;
+  }
+}
+
+int topp_max_vocab() { return kToppThreads * kToppGroups * 4; }
+
+void launch_topp_finalize(const float* logits, int M, int V, const SampleArgs& smp, float top_p,
+                          int32_t* ids_cur, int32_t* tokens, float* logp, int tok_stride,
+                          const int32_t* pos_next, int32_t* pos_dev, hipStream_t st) {
+  topp_finalize_kernel<<<M, kToppThreads, 0, st>>>(logits, V, smp, top_p, ids_cur, tokens, logp, tok_stride,
+                                                   pos_next, pos_dev);
 }
 
 // ---------------------------------------------------------------------------------

@@ -176,7 +176,8 @@ void launch_reduce_argmax(const float* parts, int S, int M, int N, float* logits
 // tokens[m * tok_stride + p] (if tokens) and d_next[m] (if non-null); with logp (and
 // smp's block sums), the pick's log-probability to logp[m * tok_stride + p]: the
 // tempered logit minus the logsumexp of the row, blocks combined in a fixed order.
-// Finally *pos_dev = p (the position the next step feeds).
+// tok_stride 0 writes tokens[m] and logp[m] instead.  Finally *pos_dev = p (the
+// position the next step feeds; skipped when pos_dev is null).
 void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, const SampleArgs& smp,
                             int n_blocks, int M, int32_t* ids_cur, int32_t* tokens, float* logp,
                             int tok_stride, const int32_t* pos_next, int32_t* pos_dev, int32_t* d_next,
@@ -189,6 +190,16 @@ void launch_argmax_finalize(const float* best_val, const int32_t* best_idx, cons
 // outside 0 .. V-1 gives NaN.
 void launch_logprob_gather(const float* logits, int rows, int V, const int32_t* seq, int S, int S_p,
                            int n, int r0, float* out, hipStream_t st);
+
+// Top-p pick of each of M rows of fp32 logits [M][V] (V <= topp_max_vocab()): the
+// Gumbel-max rule of smp (inv_temp > 0) restricted to the row's nucleus under
+// softmax(logit * inv_temp) with mass top_p (0 < top_p < 1), ties at its edge
+// included.  Position protocol, outputs and log-probability (of the untruncated
+// distribution) as launch_argmax_finalize.
+int topp_max_vocab();
+void launch_topp_finalize(const float* logits, int M, int V, const SampleArgs& smp, float top_p,
+                          int32_t* ids_cur, int32_t* tokens, float* logp, int tok_stride,
+                          const int32_t* pos_next, int32_t* pos_dev, hipStream_t st);
 
 // ---- attention ---------------------------------------------------------------------
 // Causal attention of the prompt pass: q [B*S, d] (scaled), keys/values of

@@ -56,7 +56,7 @@ class he_lora_table(ctypes.Structure):
 
 
 class he_sampling(ctypes.Structure):
-    _fields_ = [("temperature", ctypes.c_float), ("seed", ctypes.c_uint64)]
+    _fields_ = [("temperature", ctypes.c_float), ("seed", ctypes.c_uint64), ("top_p", ctypes.c_float)]
 
 
 class he_kernel_stat(ctypes.Structure):
@@ -79,6 +79,7 @@ _SIGS = {
     "he_generate": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "he_generate_ex": (_i32, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
     "he_score": (_i32, [_vp, _vp, _i32, _i32, _vp]),
+    "he_sample": (_i32, [_vp, _vp, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
     "he_logprobs": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "he_sync": (_i32, [_vp]),
     "he_last_error": (ctypes.c_char_p, [_vp]),
@@ -163,6 +164,12 @@ def he_generate_ex(ctx, d_prompt: int, B: int, S: int, S_g: int, smp, d_out: int
     """smp: he_sampling or None (greedy)."""
     p = ctypes.byref(smp) if smp is not None else None
     return _check(lib().he_generate_ex(ctx, _vp(d_prompt), B, S, S_g, p, _vp(d_out), _vp(d_logprobs or None)), ctx)
+
+
+def he_sample(ctx, d_logits: int, B: int, position: int, smp, d_tokens: int, d_logprobs: int = 0):
+    """smp: he_sampling or None (greedy)."""
+    p = ctypes.byref(smp) if smp is not None else None
+    return _check(lib().he_sample(ctx, _vp(d_logits), B, position, p, _vp(d_tokens), _vp(d_logprobs or None)), ctx)
 
 
 def he_score(ctx, d_ids: int, B: int, S: int, d_reward: int):
