@@ -216,20 +216,16 @@ __device__ __forceinline__ T* x_at(T* x, int row, int k, int d, int x_lay) {
 // variance around it, as two fixed-order block reductions; gamma and beta are
 // fetched before the reductions so their latency overlaps them.
 template <typename T>
-__device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, float eps,
-                                         const T* g, const T* b, T* x, int row, int x_lay,
-                                         float* hrow_post, float* red) {
+__device__ __forceinline__ void ln_write_pre(const float (&v)[kLnChunks][4], const float (&gv)[kLnChunks][4],
+                                             const float (&bv)[kLnChunks][4], int d, float eps, T* x,
+                                             int row, int x_lay, float* hrow_post, float* red) {
   const int tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
-  float gv[kLnChunks][4], bv[kLnChunks][4];
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < kLnChunks; ++c)
-    if (tid + c * nt < nch) {
-      ld4(g + (tid + c * nt) * 4, gv[c]);
-      ld4(b + (tid + c * nt) * 4, bv[c]);
+    if (tid + c * nt < nch)
 #pragma unroll
       for (int q = 0; q < 4; ++q) s += v[c][q];
-    }
   const float mean = block_sum(s, red) / (float)d;
   float s2 = 0.f;
 #pragma unroll
@@ -250,6 +246,21 @@ __device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, 
       st4(x_at(x, row, ch * 4, d, x_lay), y);         // GEMM input: rounded
     }
   }
+}
+
+template <typename T>
+__device__ __forceinline__ void ln_write(const float (&v)[kLnChunks][4], int d, float eps,
+                                         const T* g, const T* b, T* x, int row, int x_lay,
+                                         float* hrow_post, float* red) {
+  const int tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
+  float gv[kLnChunks][4], bv[kLnChunks][4];
+#pragma unroll
+  for (int c = 0; c < kLnChunks; ++c)
+    if (tid + c * nt < nch) {
+      ld4(g + (tid + c * nt) * 4, gv[c]);
+      ld4(b + (tid + c * nt) * 4, bv[c]);
+    }
+  ln_write_pre<T>(v, gv, bv, d, eps, x, row, x_lay, hrow_post, red);
 }
 
 // Threads per row: two chunks of 4 each (measured fastest at decode shapes), whole waves.
@@ -336,7 +347,10 @@ void launch_embed_gather(int dt, const int32_t* ids, const void* E, void* xe, in
     embed_gather_kernel<float><<<M, 256, 0, st>>>(ids, (const float*)E, (float*)xe, de, vocab);
 }
 
-// Residual update (sum of split-K partials + bias, fixed order) and LayerNorm.
+// Residual update (sum of split-K partials + bias, fixed order) and LayerNorm.  Every
+// load of the row (gamma, beta, the stream, up to kNormSplits partials and the bias)
+// is issued before any arithmetic, so the row costs one memory round trip.
+constexpr int kNormSplits = 8;
 template <typename T>
 __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
                                                     const float* __restrict__ parts, int nsplit,
@@ -349,41 +363,50 @@ __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
   const int r = blockIdx.x, tid = threadIdx.x, nch = d / 4, nt = blockDim.x;
   const size_t row = (size_t)(r / row_group) * row_stride + row_offset + r % row_group;
   float* hr = h + row * d;
-  float v[kLnChunks][4];
+  float v[kLnChunks][4], gv[kLnChunks][4], bv[kLnChunks][4];
+  const bool pre = parts && nsplit <= kNormSplits;
+  float pp[kLnChunks][kNormSplits][4], bb[kLnChunks][4];
 #pragma unroll
   for (int c = 0; c < kLnChunks; ++c) {
     const int ch = tid + c * nt;
     if (ch < nch) {
+      ld4(g + ch * 4, gv[c]);
+      ld4(b + ch * 4, bv[c]);
       ld4(hr + ch * 4, v[c]);
-      if (parts) {
-        float add[4] = {0.f, 0.f, 0.f, 0.f};
-        const float* pp = parts + (size_t)r * d + ch * 4;
-        const size_t pstride = (size_t)M * d;
-        int s = 0;
-        for (; s + 4 <= nsplit; s += 4) {          // four loads in flight, summed in order
-          float p0[4], p1[4], p2[4], p3[4];
-          ld4(pp + (s + 0) * pstride, p0);
-          ld4(pp + (s + 1) * pstride, p1);
-          ld4(pp + (s + 2) * pstride, p2);
-          ld4(pp + (s + 3) * pstride, p3);
+      if (pre) {
+        ld4(bias + ch * 4, bb[c]);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) add[q] = (((add[q] + p0[q]) + p1[q]) + p2[q]) + p3[q];
-        }
-        for (; s < nsplit; ++s) {
-          float p0[4];
-          ld4(pp + s * pstride, p0);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) add[q] += p0[q];
-        }
-        float bv[4];
-        ld4(bias + ch * 4, bv);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[c][q] += add[q] + bv[q];
-        st4(hr + ch * 4, v[c]);
+        for (int s = 0; s < kNormSplits; ++s)
+          if (s < nsplit) ld4(parts + ((size_t)s * M + r) * d + ch * 4, pp[c][s]);
       }
     }
   }
-  ln_write<T>(v, d, eps, g, b, x, r, x_lay, post ? hr : nullptr, red);
+#pragma unroll
+  for (int c = 0; c < kLnChunks; ++c) {
+    const int ch = tid + c * nt;
+    if (ch < nch && parts) {
+      float add[4] = {0.f, 0.f, 0.f, 0.f};
+      if (pre) {
+#pragma unroll
+        for (int s = 0; s < kNormSplits; ++s)
+          if (s < nsplit)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) add[q] += pp[c][s][q];
+      } else {                                    // more splits than registers: in order
+        ld4(bias + ch * 4, bb[c]);
+        for (int s = 0; s < nsplit; ++s) {
+          float p0[4];
+          ld4(parts + ((size_t)s * M + r) * d + ch * 4, p0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) add[q] += p0[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[c][q] += add[q] + bb[c][q];
+      st4(hr + ch * 4, v[c]);
+    }
+  }
+  ln_write_pre<T>(v, gv, bv, d, eps, x, r, x_lay, post ? hr : nullptr, red);
 }
 
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias, const void* g,
