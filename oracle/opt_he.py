@@ -204,7 +204,7 @@ class OracleModel:
 
     def __init__(self, shape, params: Dict, prec: Precision, lora: Optional[Dict] = None,
                  lora_scale: float = 1.0, lora_tag: str = "lora", cache_layers: bool = True,
-                 eps: float = LN_EPS):
+                 eps: float = LN_EPS, fp8_decode: bool = False):
         self.shape = shape
         self.params = params
         self.prec = prec
@@ -215,6 +215,10 @@ class OracleModel:
         self.cache_layers = cache_layers
         self._layers: Dict[int, Dict[str, np.ndarray]] = {}
         self._glob: Dict[str, np.ndarray] = {}
+        # weight-only FP8 for the decode steps' projections (oracle/fp8.py)
+        self.fp8_decode = fp8_decode
+        self._in_decode = False
+        self._layers_q: Dict[int, Dict[str, np.ndarray]] = {}
 
     # -- parameters -----------------------------------------------------------
     def g(self, name: str) -> np.ndarray:
@@ -223,6 +227,23 @@ class OracleModel:
         return self._glob[name]
 
     def layer(self, i: int) -> Dict[str, np.ndarray]:
+        if self.fp8_decode and self._in_decode:
+            return self._layer_fp8(i)
+        return self._layer_full(i)
+
+    def _layer_fp8(self, i: int) -> Dict[str, np.ndarray]:
+        """Layer i with its four projection weights replaced by their FP8 versions."""
+        from oracle import fp8
+        if i not in self._layers_q:
+            lw = dict(self._layer_full(i))
+            for name in ("qkv.w", "out.w", "fc1.w", "fc2.w"):
+                lw[name] = fp8.fp8_weight(lw[name])
+            if not self.cache_layers:
+                return lw
+            self._layers_q[i] = lw
+        return self._layers_q[i]
+
+    def _layer_full(self, i: int) -> Dict[str, np.ndarray]:
         if i in self._layers:
             return self._layers[i]
         d = self.shape.d_model
@@ -342,7 +363,11 @@ class OracleModel:
         pos = cache.length
         if pos >= cache.k[0].shape[2]:
             raise IndexError("KV cache full")
-        h = self.hidden(ids, pos, cache)
+        self._in_decode = True
+        try:
+            h = self.hidden(ids, pos, cache)
+        finally:
+            self._in_decode = False
         cache.length = pos + 1
         return self.lm_logits(h[:, -1])
 
