@@ -452,6 +452,39 @@ def main():
             "mean_logprob": float(lps.mean()), "logprobs_finite": bool((lps == lps).all())}
         log(f"sampled: {json.dumps(res['sampled'])}")
 
+        # weight-only FP8 decode (a separate mode: E4M3 projection weights, half the
+        # weight bytes per step): greedy generation beside the bf16 one, and the decode
+        # GEMVs' time per launch with their algorithmic (one byte per weight) traffic
+        with torch.cuda.stream(st):
+            he.he_fuse_lora(ctx, lt)
+            he.he_set_fp8_decode(ctx, True)
+            Ef = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            he.he_generate(ctx, prompts.data_ptr(), B, S, G, out.data_ptr())     # graph capture
+            Ef[0].record(st)
+            he.he_generate(ctx, prompts.data_ptr(), B, S, G, out.data_ptr())
+            Ef[1].record(st)
+            he.he_kernel_timer(ctx, he.HE_K_GEMV_DECODE, True)
+            he.he_generate(ctx, prompts.data_ptr(), B, S, 8, out.data_ptr())
+            gv8 = he.he_kernel_stats(ctx, he.HE_K_GEMV_DECODE)
+            he.he_kernel_timer(ctx, he.HE_K_GEMV_DECODE, False)
+            he.he_set_fp8_decode(ctx, False)
+            he.he_unfuse_lora(ctx, lt)
+            he.he_sync(ctx)
+            torch.cuda.synchronize()
+        t_f8 = Ef[0].elapsed_time(Ef[1]) / 1e3
+        L_, d_, F_ = a.n_layers, a.d_model, a.d_ffn
+        w_bf16 = L_ * (4 * d_ * d_ + 2 * d_ * F_) * 2
+        w_f8 = L_ * ((4 * d_ * d_ + 2 * d_ * F_) + 4 * (5 * d_ + F_))     # codes + per-row scales
+        f8_step_bytes = dec_bytes / (G - 1) - w_bf16 + w_f8
+        res["fp8_decode"] = {
+            "gen_ms": t_f8 * 1e3, "gen_tokens_per_s": B * G / t_f8, "vs_bf16_gen": (t_pre + t_dec) / t_f8,
+            "decode_ms_est": t_f8 * 1e3 - t_pre * 1e3,
+            "decode_bytes_per_step_avg": f8_step_bytes,
+            "decode_hbm_GBps_est": f8_step_bytes * (G - 1) / (t_f8 - t_pre) / 1e9,
+            "gemv_avg_us": gv8.total_ms / gv8.launches * 1e3 if gv8.launches else None,
+            "gemv_GBps": gv8.bytes / (gv8.total_ms / 1e3) / 1e9 if gv8.total_ms else None}
+        log(f"fp8_decode: {json.dumps(res['fp8_decode'])}")
+
         # teacher-forced scoring of the finished experience (prompt + the answer just
         # sampled, S + G tokens): log-probabilities of the B x G answer tokens, fused weights
         with torch.cuda.stream(st):

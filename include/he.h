@@ -308,6 +308,28 @@ he_status he_score(he_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t S, floa
 he_status he_logprobs(he_ctx* ctx, const int32_t* d_seq, int32_t B, int32_t S, int32_t S_p,
                       float* d_logprobs);
 
+/* Weight-only FP8 decode (Chapter 11 "System Architecture & Infrastructure at
+ * Scale", section "The Generation Bottleneck: Quantitative Analysis": 8-bit weights
+ * halve the bytes a bandwidth-bound generation step streams).  enable != 0 makes an
+ * OCP E4M3 copy of the q/k/v, out, fc1 and fc2 weights of every layer, per output
+ * channel: scale_n = max_k |W[n,k]| / 448 (float32), code = E4M3(W[n,k] / scale_n)
+ * rounded to nearest even, saturating at 448.  Decode steps then read those copies
+ * (half the weight bytes), multiplying each output row by its scale; the prompt
+ * pass, the LM head and reward scoring keep bf16.  The copy is library-owned
+ * (about 1 byte per projection weight, kept across workspace release / retake)
+ * and is remade after every he_fuse_lora / he_unfuse_lora; call again with
+ * enable != 0 after changing the weights in place.  enable == 0 frees it.  Either
+ * way a new prompt pass must precede the next decode step.
+ * Errors: HE_E_UNSUPPORTED (fp32 or scalar-head model, d or d_ffn not a multiple of
+ * 256), HE_E_OOM. */
+he_status he_set_fp8_decode(he_ctx* ctx, int32_t enable);
+
+/* The E4M3 codes of one FP8 projection copy in row-major order: proj 0 q/k/v
+ * ([3d, d]), 1 out ([d, d]), 2 fc1 ([d_ffn, d]), 3 fc2 ([d, d_ffn]); d_codes receives
+ * N x K bytes, d_scales N float32 (device, caller-owned, written by the end of the
+ * call's stream work).  Errors: HE_E_STATE (FP8 decode off), HE_E_ARG. */
+he_status he_fp8_export(he_ctx* ctx, int32_t layer, int32_t proj, uint8_t* d_codes, float* d_scales);
+
 /* Wait for the context's stream; reports deferred device faults as HE_E_HIP. */
 he_status he_sync(he_ctx* ctx);
 

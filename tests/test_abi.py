@@ -246,3 +246,28 @@ def test_reward_model_only_scores():
     assert _status(he.he_sample, ctx, P, 2, 0, None, P, 0) == he.HE_E_UNSUPPORTED
     assert _status(he.he_score, ctx, P, 129, 512, P) == he.HE_E_ARG
     e.close()
+
+
+def test_fp8_decode_switch():
+    """Weight-only FP8 decode: bf16 LM-head models with d and d_ffn divisible by 256;
+    the export needs it on and a layer / projection in range."""
+    import dataclasses
+    P = 0x1234
+    shape = dataclasses.replace(synth.WORKLOADS["opt125m"].actor, n_layers=2)
+    e = he.Engine(shape, _fake_params(shape), validate_only=True)
+    ctx = e.ctx
+    assert _status(he.he_fp8_export, ctx, 0, 0, P, P) == he.HE_E_STATE
+    he.he_set_fp8_decode(ctx, True)
+    he.he_fp8_export(ctx, 1, 3, P, P)
+    for args in ((2, 0, P, P), (0, 4, P, P), (-1, 0, P, P), (0, 0, 0, P), (0, 0, P, 0)):
+        assert _status(he.he_fp8_export, ctx, *args) == he.HE_E_ARG, args
+    he.he_set_fp8_decode(ctx, False)
+    assert _status(he.he_fp8_export, ctx, 0, 0, P, P) == he.HE_E_STATE
+    e.close()
+    for bad in (synth.WORKLOADS["tiny"].actor,                                          # fp32
+                dataclasses.replace(shape, d_model=640, n_heads=10),                     # d % 256
+                dataclasses.replace(shape, d_ffn=2944),                                  # d_ffn % 256
+                synth.WORKLOADS["opt13b"].reward):                                       # scalar head
+        e = he.Engine(bad, _fake_params(bad), validate_only=True)
+        assert _status(he.he_set_fp8_decode, e.ctx, True) == he.HE_E_UNSUPPORTED, bad
+        e.close()

@@ -105,6 +105,16 @@ __device__ __forceinline__ size_t xt_off(int m, int k, int mt) {
   return ((size_t)((k >> 5) * mt + (m >> 4)) << 9) + (((m & 15) | (((k >> 3) & 3) << 4)) << 3) + (k & 7);
 }
 
+// FP8 (E4M3) decode-weight layout of W [N][K] (N % 16 == 0, K % 64 == 0): blocks of
+// 16 rows x 64 k, 1 KB each, row block major then k, so a row block's whole K range
+// is contiguous.  Lane l of a block holds row l % 16 and, in its 16 bytes, k 8 (l / 16)
+// .. + 8 of the block's first 32-wide k-step (bytes 0..7) and of its second (bytes
+// 8..15): one 16-byte load per lane gives the MFMA A operands of two k-steps.
+__device__ __forceinline__ size_t f8_off(int n, int k, int K) {
+  return ((size_t)(n >> 4) * (K >> 6) + (k >> 6)) * 1024 + (((n & 15) + 16 * ((k & 31) >> 3)) << 4) +
+         (k & 7) + 8 * ((k >> 5) & 1);
+}
+
 // Activation layout code of a [M][K] storage-type matrix: 0 row-major; mt > 0 the
 // decode fragment tiling with mt row tiles (xt_off); -il < 0 the inference layout with
 // block width 2^il over K (il_off, as for weights), the prompt-pass GEMM operand.

@@ -20,6 +20,7 @@
 #include <cstring>
 #include <string>
 #include <utility>
+#include <array>
 #include <vector>
 
 #include "../../include/he.h"
@@ -118,6 +119,15 @@ struct he_ctx {
 
   Timer timers[HE_K_COUNT];
   bool fail_next_alloc = false, fail_next_step = false;
+
+  // weight-only FP8 decode: E4M3 copies (f8_off layout) and per-row scales of the four
+  // projections of every layer, in one library-owned allocation kept across
+  // workspace release / retake
+  bool f8_on = false;
+  bool graph_f8 = false;
+  char* f8buf = nullptr;
+  struct F8Layer { uint8_t* q[4]; float* s[4]; };
+  std::vector<F8Layer> f8;
 };
 
 // ------------------------------------------------------------------------------------
@@ -205,10 +215,11 @@ static bool any_timer_armed(const he_ctx* c) {
 }
 
 static void set_plans(he_ctx* c, int B) {
-  c->p_qkv = decode_plan(c->dt, B, 3 * c->d, c->d, true, c->dt == DT_BF16);   // bf16: fused QKV epilogue
-  c->p_out = decode_plan(c->dt, B, c->d, c->d, true);
-  c->p_fc1 = decode_plan(c->dt, B, c->F, c->d, true);
-  c->p_fc2 = decode_plan(c->dt, B, c->d, c->F, true);
+  const bool f8 = c->f8_on;
+  c->p_qkv = decode_plan(c->dt, B, 3 * c->d, c->d, true, c->dt == DT_BF16, f8);   // bf16: fused QKV epilogue
+  c->p_out = decode_plan(c->dt, B, c->d, c->d, true, false, f8);
+  c->p_fc1 = decode_plan(c->dt, B, c->F, c->d, true, false, f8);
+  c->p_fc2 = decode_plan(c->dt, B, c->d, c->F, true, false, f8);
   c->p_lm = decode_plan(c->dt, B, c->V, c->d, true, true);
   c->xmt = c->dt == DT_BF16 ? decode_mt(B) : 0;
   c->n_argmax_blocks = gemv_argmax_blocks(c->dt, c->p_lm, c->V);
@@ -220,11 +231,14 @@ static size_t parts_elems(he_ctx* c, int max_batch, int* argmax_cap) {
   size_t need = 0;
   int nb = 0;
   auto room = [&](const GemvPlan& p, int B, int N) { return (size_t)p.splits * (size_t)B * (size_t)N; };
+  for (int B = 1; B <= max_batch; ++B)
+    for (bool f8 : {false, c->dt == DT_BF16}) {   // plans with and without E4M3 weights
+      need = std::max(need, room(decode_plan(c->dt, B, 3 * c->d, c->d, true, c->dt == DT_BF16, f8), B, 3 * c->d));
+      need = std::max(need, room(decode_plan(c->dt, B, c->d, c->d, true, false, f8), B, c->d));
+      need = std::max(need, room(decode_plan(c->dt, B, c->F, c->d, true, false, f8), B, c->F));
+      need = std::max(need, room(decode_plan(c->dt, B, c->d, c->F, true, false, f8), B, c->d));
+    }
   for (int B = 1; B <= max_batch; ++B) {
-    need = std::max(need, room(decode_plan(c->dt, B, 3 * c->d, c->d, true, c->dt == DT_BF16), B, 3 * c->d));
-    need = std::max(need, room(decode_plan(c->dt, B, c->d, c->d, true), B, c->d));
-    need = std::max(need, room(decode_plan(c->dt, B, c->F, c->d, true), B, c->F));
-    need = std::max(need, room(decode_plan(c->dt, B, c->d, c->F, true), B, c->d));
     const GemvPlan lm = decode_plan(c->dt, B, c->V, c->d, true, true);
     need = std::max(need, room(lm, B, c->V));
     nb = std::max(nb, gemv_argmax_blocks(c->dt, lm, c->V));
@@ -263,10 +277,11 @@ static const void* ln_b_after(he_ctx* c, int l) {
 
 // One decode projection into split-K partials (plan p).
 static void decode_partials(he_ctx* c, const void* X, const void* W, int B, int N, int K,
-                            const GemvPlan& p, int il, hipStream_t st) {
+                            const GemvPlan& p, int il, hipStream_t st, const float* w_scale = nullptr) {
   GemvArgs g;
   g.out_mode = GV_PARTIAL;
   g.w_il = il;
+  g.w_scale = w_scale;
   g.parts = c->parts;
   launch_gemv(c->dt, X, W, B, N, K, p, g, st);
 }
@@ -393,13 +408,24 @@ static void enqueue_step(he_ctx* c, int B, bool want_logits, int pos) {
   });
   for (int l = 0; l < c->L; ++l) {
     const he_layer_weights& w = c->layers[l];
+    // the four projections' weights: bf16, or their E4M3 copies with per-row scales
+    const bool f8 = c->f8_on;
+    const void* Wq = f8 ? (const void*)c->f8[l].q[0] : w.w_qkv;
+    const void* Wo = f8 ? (const void*)c->f8[l].q[1] : w.w_out;
+    const void* W1 = f8 ? (const void*)c->f8[l].q[2] : w.w_fc1;
+    const void* W2 = f8 ? (const void*)c->f8[l].q[3] : w.w_fc2;
+    const float* Sq = f8 ? c->f8[l].s[0] : nullptr;
+    const float* So = f8 ? c->f8[l].s[1] : nullptr;
+    const float* S1 = f8 ? c->f8[l].s[2] : nullptr;
+    const float* S2 = f8 ? c->f8[l].s[3] : nullptr;
+    const double wb = f8 ? 1.0 : (double)es;   // weight bytes per element
     if (dt == DT_BF16) {   // q, k, v finished in the projection's epilogue
       GemvArgs g;
-      g.out_mode = GV_QKV; g.w_il = w_il(c, d); g.bias = w.b_qkv;
+      g.out_mode = GV_QKV; g.w_il = w_il(c, d); g.bias = w.b_qkv; g.w_scale = Sq;
       g.q_out = c->q; g.k_cache = kcache(c, l); g.v_cache = vcache(c, l); g.pos_dev = c->pos_dev;
       g.d = d; g.H = c->H; g.D = c->D; g.S_max = c->max_seq; g.q_scale = c->q_scale;
-      run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * es, 2.0 * B * 3 * d * d,
-            [&] { launch_gemv(dt, c->x, w.w_qkv, B, 3 * d, d, c->p_qkv, g, st); });
+      run_k(c, HE_K_GEMV_DECODE, (double)3 * d * d * wb, 2.0 * B * 3 * d * d,
+            [&] { launch_gemv(dt, c->x, Wq, B, 3 * d, d, c->p_qkv, g, st); });
       run_k(c, HE_K_ATTN_DECODE, 2.0 * B * d * es * (double)(pos + 1), 4.0 * B * d * (double)(pos + 1), [&] {
         launch_attn_decode_q(dt, c->q, kcache(c, l), vcache(c, l), c->pos_dev, c->o, B, c->H, c->D,
                              c->max_seq, xmt, st);
@@ -412,25 +438,25 @@ static void enqueue_step(he_ctx* c, int B, bool want_logits, int pos) {
                            c->o, B, c->H, c->D, c->max_seq, c->q_scale, xmt, st);
       });
     }
-    run_k(c, HE_K_GEMV_DECODE, (double)d * d * es, 2.0 * B * d * d,
-          [&] { decode_partials(c, c->o, w.w_out, B, d, d, c->p_out, w_il(c, d), st); });
+    run_k(c, HE_K_GEMV_DECODE, (double)d * d * wb, 2.0 * B * d * d,
+          [&] { decode_partials(c, c->o, Wo, B, d, d, c->p_out, w_il(c, d), st, So); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
       launch_norm(dt, c->h, c->parts, c->p_out.splits, w.b_out, w.ln2_g, w.ln2_b, eps, c->x, B, d, 1, 0, 0,
                   xmt, st);
     });
     if (dt == DT_BF16 && c->p_fc1.splits > 1) {
-      run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
-            [&] { decode_partials(c, c->x, w.w_fc1, B, F, d, c->p_fc1, w_il(c, d), st); });
+      run_k(c, HE_K_GEMV_DECODE, (double)F * d * wb, 2.0 * B * F * d,
+            [&] { decode_partials(c, c->x, W1, B, F, d, c->p_fc1, w_il(c, d), st, S1); });
       run_k(c, HE_K_EMBED_NORM, (double)B * F * 4 * c->p_fc1.splits, 0,
             [&] { launch_reduce_relu(c->parts, c->p_fc1.splits, w.b_fc1, c->a, B, F, xmt, st); });
     } else {
       GemvArgs g1;
-      g1.out_mode = GV_RELU; g1.w_il = w_il(c, d); g1.bias = w.b_fc1; g1.out = c->a;
-      run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
-            [&] { launch_gemv(dt, c->x, w.w_fc1, B, F, d, c->p_fc1, g1, st); });
+      g1.out_mode = GV_RELU; g1.w_il = w_il(c, d); g1.bias = w.b_fc1; g1.out = c->a; g1.w_scale = S1;
+      run_k(c, HE_K_GEMV_DECODE, (double)F * d * wb, 2.0 * B * F * d,
+            [&] { launch_gemv(dt, c->x, W1, B, F, d, c->p_fc1, g1, st); });
     }
-    run_k(c, HE_K_GEMV_DECODE, (double)F * d * es, 2.0 * B * F * d,
-          [&] { decode_partials(c, c->a, w.w_fc2, B, d, F, c->p_fc2, w_il(c, F), st); });
+    run_k(c, HE_K_GEMV_DECODE, (double)F * d * wb, 2.0 * B * F * d,
+          [&] { decode_partials(c, c->a, W2, B, d, F, c->p_fc2, w_il(c, F), st, S2); });
     run_k(c, HE_K_EMBED_NORM, (double)B * d * 8, 0, [&] {
       launch_norm(dt, c->h, c->parts, c->p_fc2.splits, w.b_fc2, ln_g_after(c, l), ln_b_after(c, l), eps,
                   c->x, B, d, 1, 0, 0, xmt, st);
@@ -625,6 +651,7 @@ he_status he_release_cache(he_ctx* c) {
 he_status he_destroy(he_ctx* c) {
   if (!c) return HE_OK;
   he_status s = he_release_cache(c);
+  if (c->f8buf) hipFree(c->f8buf);
   if (!c->validate_only) {
     for (Timer& t : c->timers) {
       for (auto& p : t.live) { hipEventDestroy(p.first); hipEventDestroy(p.second); }
@@ -634,6 +661,85 @@ he_status he_destroy(he_ctx* c) {
   }
   delete c;
   return s;
+}
+
+// E4M3 copies of the current projection weights (in whatever layout they hold now).
+static he_status f8_requantize(he_ctx* c) {
+  if (!c->f8_on || c->validate_only) return HE_OK;
+  const int d = c->d, F = c->F;
+  for (int l = 0; l < c->L; ++l) {
+    const he_layer_weights& w = c->layers[l];
+    launch_quantize_fp8(w.w_qkv, 3 * d, d, w_il(c, d), c->f8[l].q[0], c->f8[l].s[0], c->stream);
+    launch_quantize_fp8(w.w_out, d, d, w_il(c, d), c->f8[l].q[1], c->f8[l].s[1], c->stream);
+    launch_quantize_fp8(w.w_fc1, F, d, w_il(c, d), c->f8[l].q[2], c->f8[l].s[2], c->stream);
+    launch_quantize_fp8(w.w_fc2, d, F, w_il(c, F), c->f8[l].q[3], c->f8[l].s[3], c->stream);
+  }
+  return check_launch(c, "fp8 quantisation launch");
+}
+
+he_status he_set_fp8_decode(he_ctx* c, int32_t enable) {
+  if (!c) return HE_E_ARG;
+  if (c->failed) return set_err(c, HE_E_HIP, "context failed earlier: %s", c->err.c_str());
+  c->prefilled = false;   // decode plans depend on the weight format: a new prompt pass
+  if (!enable) {
+    if (c->f8buf && !c->validate_only) {
+      HIP_TRY(c, hipStreamSynchronize(c->stream));
+      hipFree(c->f8buf);
+    }
+    c->f8buf = nullptr;
+    c->f8.clear();
+    c->f8_on = false;
+    return HE_OK;
+  }
+  if (c->dt != DT_BF16 || c->desc.head != HE_HEAD_LM)
+    return set_err(c, HE_E_UNSUPPORTED, "FP8 decode weights need a bf16 LM-head model");
+  if (c->d % 256 || c->F % 256)
+    return set_err(c, HE_E_UNSUPPORTED, "FP8 decode weights need d and d_ffn divisible by 256");
+  if (c->f8_on) return f8_requantize(c);
+  const int d = c->d, F = c->F;
+  const size_t nq[4] = {(size_t)3 * d * d, (size_t)d * d, (size_t)F * d, (size_t)d * F};
+  const size_t ns[4] = {(size_t)3 * d, (size_t)d, (size_t)F, (size_t)d};
+  size_t off = 0;
+  std::vector<std::array<size_t, 8>> offs(c->L);
+  for (int l = 0; l < c->L; ++l)
+    for (int j = 0; j < 4; ++j) {
+      offs[l][j] = off; off += (nq[j] + 255) / 256 * 256;
+      offs[l][4 + j] = off; off += (ns[j] * 4 + 255) / 256 * 256;
+    }
+  if (c->validate_only) {
+    c->f8_on = true;
+    return HE_OK;
+  }
+  char* buf = nullptr;
+  hipError_t e = hipMalloc((void**)&buf, std::max<size_t>(off, 256));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return set_err(c, HE_E_OOM, "FP8 weight allocation of %zu bytes failed: %s", off, hipGetErrorString(e));
+  }
+  c->f8buf = buf;
+  c->f8.resize(c->L);
+  for (int l = 0; l < c->L; ++l)
+    for (int j = 0; j < 4; ++j) {
+      c->f8[l].q[j] = (uint8_t*)(buf + offs[l][j]);
+      c->f8[l].s[j] = (float*)(buf + offs[l][4 + j]);
+    }
+  c->f8_on = true;
+  return f8_requantize(c);
+}
+
+he_status he_fp8_export(he_ctx* c, int32_t layer, int32_t proj, uint8_t* d_codes, float* d_scales) {
+  if (!c) return HE_E_ARG;
+  if (!c->f8_on) return set_err(c, HE_E_STATE, "FP8 decode weights are off");
+  if (layer < 0 || layer >= c->L || proj < 0 || proj > 3)
+    return set_err(c, HE_E_ARG, "layer %d / projection %d out of range", layer, proj);
+  if (!d_codes || !d_scales) return set_err(c, HE_E_ARG, "NULL buffer");
+  if (c->validate_only) return HE_OK;
+  const int d = c->d, F = c->F;
+  const int N[4] = {3 * d, d, F, d}, K[4] = {d, d, d, F};
+  launch_fp8_rowmajor(c->f8[layer].q[proj], N[proj], K[proj], d_codes, c->stream);
+  HIP_TRY(c, hipMemcpyAsync(d_scales, c->f8[layer].s[proj], (size_t)N[proj] * 4, hipMemcpyDeviceToDevice,
+                            c->stream));
+  return check_launch(c, "fp8 export launch");
 }
 
 static he_status lora_common(he_ctx* c, const he_lora_table* t, float sign) {
@@ -683,6 +789,7 @@ he_status he_fuse_lora(he_ctx* c, const he_lora_table* t) {
   if (c->fused) return set_err(c, HE_E_STATE, "LoRA already fused");
   he_status s = lora_common(c, t, +1.f);
   if (s == HE_OK) c->fused = true;
+  if (s == HE_OK) s = f8_requantize(c);
   return s;
 }
 
@@ -691,6 +798,7 @@ he_status he_unfuse_lora(he_ctx* c, const he_lora_table* t) {
   if (!c->fused) return set_err(c, HE_E_STATE, "LoRA not fused");
   he_status s = lora_common(c, t, -1.f);
   if (s == HE_OK) c->fused = false;
+  if (s == HE_OK) s = f8_requantize(c);
   return s;
 }
 
@@ -866,7 +974,8 @@ static he_status run_step(he_ctx* c, bool want_logits) {
   if (graph) {
     hipGraphExec_t& ge = c->graph[want_logits ? 1 : 0];
     if (c->graph_B != B || c->graph_fused != c->fused || c->graph_itemp != c->inv_temp ||
-        c->graph_seed != c->seed || c->graph_logp != c->want_logp || c->graph_topp != c->top_p)
+        c->graph_seed != c->seed || c->graph_logp != c->want_logp || c->graph_topp != c->top_p ||
+        c->graph_f8 != c->f8_on)
       drop_graphs(c);
     if (!ge) {
       hipGraph_t g = nullptr;
@@ -885,6 +994,7 @@ static he_status run_step(he_ctx* c, bool want_logits) {
       c->graph_seed = c->seed;
       c->graph_logp = c->want_logp;
       c->graph_topp = c->top_p;
+      c->graph_f8 = c->f8_on;
     }
     HIP_TRY(c, hipGraphLaunch(ge, c->stream));
   } else {

@@ -47,9 +47,10 @@ int decode_mt(int M) { return pow2_ceil((M + 15) / 16); }
 // to 1024 k), then the most rows per wave (fewer activation loads per weight byte)
 // that still puts >= 512 waves in flight, then as many waves per WG (fewer partials)
 // as keeps the WG count a multiple of the 256 CUs or >= 1024.  `whole` asks for a
-// single partial group (the fused bias+ReLU and argmax epilogues).  fp32: a split
-// over K.
-GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole) {
+// single partial group (the fused bias+ReLU and argmax epilogues).  `f8` (E4M3
+// weights) asks for K ranges that are multiples of 256 (eight k-steps per loop
+// iteration).  fp32: a split over K.
+GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole, bool f8) {
   GemvPlan p;
   if (dt != DT_BF16) {
     p.splits = allow_split ? std::max(1, std::min(K / 256, 8)) : 1;
@@ -90,21 +91,22 @@ GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole) 
       const long cost = (rows(fr) + 255) / 256 * fr;
       if (best_cost < 0 || cost < best_cost) { best_cost = cost; best_fr = fr; }
     }
+    const int kq = f8 ? 256 : 128;
     int nwk = 1;
-    while (nwk < 4 && rows(best_fr) * nwk < 1024 && K % (128 * nwk * 2) == 0) nwk *= 2;
-    if (K % (128 * nwk) == 0) {
+    while (nwk < 4 && rows(best_fr) * nwk < 1024 && K % (kq * nwk * 2) == 0) nwk *= 2;
+    if (K % (kq * nwk) == 0) {
       p.fr = best_fr; p.nwk = nwk; p.kr = K / nwk; p.splits = 1;
       return p;
     }
   }
   if (allow_split) {
-    for (int kr = 1024; kr >= 128; kr >>= 1)
+    for (int kr = 1024; kr >= (f8 ? 256 : 128); kr >>= 1)
       if (K % kr == 0 && choose(kr, true)) return p;
   }
   // small matrices: as many waves as the shortest K range gives (K % 128 == 0 is
-  // required of bf16 models)
+  // required of bf16 models, K % 256 == 0 of E4M3 weights)
   p.fr = 1; p.nwk = 1;
-  p.kr = allow_split ? 128 : K;
+  p.kr = allow_split ? (f8 ? 256 : 128) : K;
   p.splits = K / p.kr;
   return p;
 }
@@ -149,21 +151,106 @@ struct IlArgs {
   const int32_t* pos_dev;
   int d, H, D, S_max;
   float q_scale;
+  const float* wscale;            // FP8 weights: per-row scales (W is then E4M3 in f8_off layout)
 };
 
 constexpr int kPD = 3;            // k-steps of loads in flight ahead of the MFMAs
 constexpr int kNB = kPD + 1;      // ring slots
 
-template <int MT, int FR, int NWK, int OUT>
+// Eight E4M3 codes (two words) as the bf16 A operand of one k-step: exact, since
+// every E4M3 value is a bf16 value (gfx950 packed conversion, scale 1).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true);
+  const auto q0 = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const auto q1 = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int MT, int FR, int NWK, int OUT, bool F8 = false>
 __global__ __launch_bounds__(NWK * 64) void gemv_il_kernel(const bf16* __restrict__ X,
                                                            const bf16* __restrict__ W, IlArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nrb = a.N >> 4, rb0 = blockIdx.x * FR;
   const int s0 = (blockIdx.y * NWK + wv) * a.ns;
-  bf16x8 w[kNB][FR], x[kNB][MT];
   int wrb[FR];
 #pragma unroll
   for (int f = 0; f < FR; ++f) wrb[f] = min(rb0 + f, nrb - 1);
+  f32x4 acc[FR][MT];
+#pragma unroll
+  for (int f = 0; f < FR; ++f)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (F8) {
+    // E4M3 weights: one 16-byte load per lane and fragment covers k-steps 2u and 2u + 1
+    // (double step u), so W is loaded with every other k-step.  Activations keep the
+    // k-step ring of kNB slots; double steps rotate through 4 slots.  Eight k-steps per
+    // iteration (a.ns % 8 == 0) keep every slot index fixed: at step i of an iteration
+    // the loads of step i + kPD are issued (its activations, and for even steps the
+    // double step), then step i multiplies from slot i % 4 and double slot i / 2.
+    const uint8_t* W8 = reinterpret_cast<const uint8_t*>(W);
+    const size_t k64 = (size_t)(a.K >> 6);
+    bf16x8 xs[kNB][MT];
+    uint4 w8[4][FR];
+    auto load_x = [&](int j, auto slot) {
+      const int s = s0 + j;
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        xs[slot][t] = *reinterpret_cast<const bf16x8*>(X + ((size_t)(s * MT + t) << 9) + lane * 8);
+    };
+    auto load_w = [&](int j, auto slot) {     // the double step holding k-step j (j even)
+      const size_t u = (size_t)((s0 + j) >> 1);
+#pragma unroll
+      for (int f = 0; f < FR; ++f)
+        w8[slot][f] = *reinterpret_cast<const uint4*>(W8 + ((size_t)wrb[f] * k64 + u) * 1024 + lane * 16);
+    };
+    auto mma8 = [&](auto xslot, auto wslot, auto half) {
+#pragma unroll
+      for (int f = 0; f < FR; ++f) {
+        const uint4 q = w8[wslot][f];
+        const bf16x8 wa = half ? e4m3x8_to_bf16(q.z, q.w) : e4m3x8_to_bf16(q.x, q.y);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xs[xslot][t], acc[f][t], 0, 0, 0);
+      }
+    };
+    load_w(0, std::integral_constant<int, 0>{});
+    load_x(0, std::integral_constant<int, 0>{});
+    load_x(1, std::integral_constant<int, 1>{});
+    load_w(2, std::integral_constant<int, 1>{});
+    load_x(2, std::integral_constant<int, 2>{});
+    int j0 = 0;
+    for (; j0 + 8 < a.ns; j0 += 8) {
+      static_for<8>([&](auto i) {
+        constexpr int la = i + kPD;                          // step whose loads go now
+        if constexpr ((la & 1) == 0) load_w(j0 + la, std::integral_constant<int, (la / 2) % 4>{});
+        load_x(j0 + la, std::integral_constant<int, la % kNB>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mma8(std::integral_constant<int, i % kNB>{}, std::integral_constant<int, (i / 2) % 4>{},
+             std::integral_constant<int, i & 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    static_for<8>([&](auto i) {                                // the last eight steps
+      constexpr int la = i + kPD;
+      if constexpr (la < 8) {
+        if constexpr ((la & 1) == 0) load_w(j0 + la, std::integral_constant<int, (la / 2) % 4>{});
+        load_x(j0 + la, std::integral_constant<int, la % kNB>{});
+      }
+      mma8(std::integral_constant<int, i % kNB>{}, std::integral_constant<int, (i / 2) % 4>{},
+           std::integral_constant<int, i & 1>{});
+    });
+    // per-row scales: the fragment's lane holds rows 16 rb + 4 (lane / 16) + r
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(a.wscale + wrb[f] * 16 + (lane >> 4) * 4);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[f][t] *= sc;
+    }
+  } else {
+  bf16x8 w[kNB][FR], x[kNB][MT];
   auto load = [&](int j, auto slot) {      // k-step s0 + j into ring slot `slot`
     const int s = s0 + j;
 #pragma unroll
@@ -173,11 +260,6 @@ __global__ __launch_bounds__(NWK * 64) void gemv_il_kernel(const bf16* __restric
     for (int t = 0; t < MT; ++t)
       x[slot][t] = *reinterpret_cast<const bf16x8*>(X + ((size_t)(s * MT + t) << 9) + lane * 8);
   };
-  f32x4 acc[FR][MT];
-#pragma unroll
-  for (int f = 0; f < FR; ++f)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto mma = [&](auto slot) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -200,6 +282,7 @@ __global__ __launch_bounds__(NWK * 64) void gemv_il_kernel(const bf16* __restric
   }
   load(j0 + kPD, std::integral_constant<int, kPD>{});
   static_for<kNB>([&](auto i) { mma(i); });
+  }
 
   // D fragment: lane holds rows n = 16 rb + 4 (lane / 16) + r of batch row 16 t + lane % 16.
   __shared__ f32x4 red[NWK > 1 || OUT == GV_ARGMAX ? NWK : 1][FR * MT][64];
@@ -326,6 +409,12 @@ static void il_launch(int out, const bf16* X, const bf16* W, const IlArgs& a, in
                       hipStream_t st) {
   dim3 grid((a.N / 16 + FR - 1) / FR, splits);
   const dim3 block(NWK * 64);
+  if (a.wscale) {                 // E4M3 weights (no LM head: it keeps bf16)
+    if (out == GV_PARTIAL) timed_launch(gemv_il_kernel<MT, FR, NWK, GV_PARTIAL, true>, grid, block, st, X, W, a);
+    else if (out == GV_RELU) timed_launch(gemv_il_kernel<MT, FR, NWK, GV_RELU, true>, grid, block, st, X, W, a);
+    else timed_launch(gemv_il_kernel<MT, FR, NWK, GV_QKV, true>, grid, block, st, X, W, a);
+    return;
+  }
   if (out == GV_PARTIAL) timed_launch(gemv_il_kernel<MT, FR, NWK, GV_PARTIAL>, grid, block, st, X, W, a);
   else if (out == GV_RELU) timed_launch(gemv_il_kernel<MT, FR, NWK, GV_RELU>, grid, block, st, X, W, a);
   else if (out == GV_QKV) timed_launch(gemv_il_kernel<MT, FR, NWK, GV_QKV>, grid, block, st, X, W, a);
@@ -498,6 +587,7 @@ void launch_gemv(int dt, const void* X, const void* W, int M, int N, int K, cons
     a.best_lg = g.smp.best_lg; a.blk_max = g.smp.blk_max; a.blk_sum = g.smp.blk_sum;
     a.q_out = (bf16*)g.q_out; a.k_cache = (bf16*)g.k_cache; a.v_cache = (bf16*)g.v_cache;
     a.pos_dev = g.pos_dev; a.d = g.d; a.H = g.H; a.D = g.D; a.S_max = g.S_max; a.q_scale = g.q_scale;
+    a.wscale = g.w_scale;
     const bf16* x = (const bf16*)X;
     const bf16* w = (const bf16*)W;
     switch (p.mt) {

@@ -110,7 +110,7 @@ struct GemvPlan {
 };
 // Row tiles of 16 the decode activations use for batch M (a power of two).
 int decode_mt(int M);
-GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole = false);
+GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole = false, bool f8 = false);
 
 // Pick rule of the LM head.  inv_temp == 0: greedy (largest logit, lowest index on
 // ties).  inv_temp > 0: the Gumbel-max sample of softmax(logit * inv_temp): largest
@@ -130,6 +130,9 @@ struct SampleArgs {
 struct GemvArgs {
   int out_mode = GV_PARTIAL;
   int w_il = 0;                   // bf16 W: 0 row-major, else the inference layout il_of(K)
+  // non-null: W holds E4M3 codes in the f8_off layout and these are its per-row scales
+  // (bf16 models, not GV_ARGMAX; the plan's K range a multiple of 256)
+  const float* w_scale = nullptr;
   float* parts = nullptr;         // GV_PARTIAL: [splits][M][N] fp32 (no bias)
   const void* bias = nullptr;     // GV_RELU
   void* out = nullptr;            // GV_RELU: bf16 fragment-tiled (plan mt); fp32 [M, N]
@@ -200,6 +203,13 @@ int topp_max_vocab();
 void launch_topp_finalize(const float* logits, int M, int V, const SampleArgs& smp, float top_p,
                           int32_t* ids_cur, int32_t* tokens, float* logp, int tok_stride,
                           const int32_t* pos_next, int32_t* pos_dev, hipStream_t st);
+
+// ---- weight-only FP8 decode weights ---------------------------------------------
+// Per-output-channel E4M3 codes of bf16 W [N][K] (layout w_il, N % 16 == 0,
+// K % 64 == 0) into q (f8_off layout, N K bytes) and scale [N] (amax / 448).
+void launch_quantize_fp8(const void* W, int N, int K, int w_il, uint8_t* q, float* scale, hipStream_t st);
+// The codes of q back in row-major order [N][K].
+void launch_fp8_rowmajor(const uint8_t* q, int N, int K, uint8_t* out, hipStream_t st);
 
 // ---- attention ---------------------------------------------------------------------
 // Causal attention of the prompt pass: q [B*S, d] (scaled), keys/values of

@@ -80,6 +80,8 @@ _SIGS = {
     "he_generate_ex": (_i32, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
     "he_score": (_i32, [_vp, _vp, _i32, _i32, _vp]),
     "he_sample": (_i32, [_vp, _vp, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
+    "he_set_fp8_decode": (_i32, [_vp, _i32]),
+    "he_fp8_export": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "he_logprobs": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "he_sync": (_i32, [_vp]),
     "he_last_error": (ctypes.c_char_p, [_vp]),
@@ -170,6 +172,14 @@ def he_sample(ctx, d_logits: int, B: int, position: int, smp, d_tokens: int, d_l
     """smp: he_sampling or None (greedy)."""
     p = ctypes.byref(smp) if smp is not None else None
     return _check(lib().he_sample(ctx, _vp(d_logits), B, position, p, _vp(d_tokens), _vp(d_logprobs or None)), ctx)
+
+
+def he_set_fp8_decode(ctx, enable: bool):
+    return _check(lib().he_set_fp8_decode(ctx, 1 if enable else 0), ctx)
+
+
+def he_fp8_export(ctx, layer: int, proj: int, d_codes: int, d_scales: int):
+    return _check(lib().he_fp8_export(ctx, layer, proj, _vp(d_codes), _vp(d_scales)), ctx)
 
 
 def he_score(ctx, d_ids: int, B: int, S: int, d_reward: int):
