@@ -151,3 +151,42 @@ def test_opt125m_fp8_generation_graph_replay_and_requantisation():
     assert np.array_equal(outs["graph"], outs["direct"])
     assert np.array_equal(outs["graph"], outs["after"])
     assert not np.array_equal(outs["graph"], outs["bf16"])
+
+
+def test_opt125m_fp8_top_p_generation_follows_the_rule_each_step():
+    """FP8 decode with top-p sampling: the loop's picks and log-probabilities equal
+    he_sample applied to the teacher-forced FP8 decode logits, step by step."""
+    wl = synth.WORKLOADS["opt125m"]
+    params = synth.model_params(wl.actor)
+    lora = synth.lora_params(wl.actor, wl.lora_rank)
+    B, S, G = wl.batch, wl.prompt_len, 10
+    smp = he.he_sampling(0.9, 404, 0.9)
+    run = GpuRun(wl, params)
+    lt = run.lora(lora)
+    prompts = synth.prompts(wl).cuda()
+    toks = torch.empty(B, G, dtype=torch.int32, device="cuda")
+    lps = torch.empty(B, G, dtype=torch.float32, device="cuda")
+    lg = torch.empty(B, wl.actor.vocab, dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    rt = torch.empty(B, dtype=torch.int32, device="cuda")
+    rl = torch.empty(B, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    bt, bl = [], []
+    with torch.cuda.stream(run.stream):
+        he.he_fuse_lora(run.ctx, lt)
+        he.he_set_fp8_decode(run.ctx, True)
+        he.he_retake_cache(run.ctx, B, wl.max_seq)
+        he.he_generate_ex(run.ctx, prompts.data_ptr(), B, S, G, smp, toks.data_ptr(), lps.data_ptr())
+        he.he_prefill(run.ctx, prompts.data_ptr(), B, S, nxt.data_ptr(), lg.data_ptr())
+        for j in range(G):
+            if j:
+                col = toks[:, j - 1].contiguous()
+                he.he_decode_step(run.ctx, col.data_ptr(), nxt.data_ptr(), lg.data_ptr())
+            he.he_sample(run.ctx, lg.data_ptr(), B, S + j, smp, rt.data_ptr(), rl.data_ptr())
+            he.he_sync(run.ctx)
+            bt.append(rt.cpu().numpy().copy())
+            bl.append(rl.cpu().numpy().copy())
+    a_t, a_l = toks.cpu().numpy(), lps.cpu().numpy()
+    run.close()
+    assert np.array_equal(a_t, np.stack(bt, axis=1))
+    assert np.array_equal(a_l.view(np.uint32), np.stack(bl, axis=1).view(np.uint32))

@@ -254,3 +254,58 @@ def test_opt125m_top_p_reproducible_and_limits(c2):
     g_tok, _ = _run(C2, params, lora, prompts_cpu, G, None, 0, want_lp=False)
     z_tok, _ = _run(C2, params, lora, prompts_cpu, G, 0.9, 77, top_p=1e-6)
     assert np.array_equal(g_tok, z_tok)
+
+
+def test_tiny_top_p_generation_follows_the_rule_each_step():
+    """fp32 model, a 512-token vocabulary (fewer columns than the nucleus kernel's
+    threads hold): the decode loop's top-p picks equal he_sample's at every step."""
+    wl = synth.WORKLOADS["tiny"]
+    params = synth.model_params(wl.actor)
+    lora = synth.lora_params(wl.actor, wl.lora_rank)
+    B, S, G = wl.batch, wl.prompt_len, wl.gen_len
+    smp = he.he_sampling(1.2, 31, 0.6)
+    run = GpuRun(wl, params)
+    lt = run.lora(lora)
+    prompts = synth.prompts(wl).cuda()
+    toks = torch.empty(B, G, dtype=torch.int32, device="cuda")
+    lps = torch.empty(B, G, dtype=torch.float32, device="cuda")
+    lg = torch.empty(B, wl.actor.vocab, dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    rt = torch.empty(B, dtype=torch.int32, device="cuda")
+    rl = torch.empty(B, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    bt, bl = [], []
+    with torch.cuda.stream(run.stream):
+        he.he_fuse_lora(run.ctx, lt)
+        he.he_retake_cache(run.ctx, B, wl.max_seq)
+        he.he_generate_ex(run.ctx, prompts.data_ptr(), B, S, G, smp, toks.data_ptr(), lps.data_ptr())
+        he.he_prefill(run.ctx, prompts.data_ptr(), B, S, nxt.data_ptr(), lg.data_ptr())
+        for j in range(G):
+            if j:
+                col = toks[:, j - 1].contiguous()
+                he.he_decode_step(run.ctx, col.data_ptr(), nxt.data_ptr(), lg.data_ptr())
+            he.he_sample(run.ctx, lg.data_ptr(), B, S + j, smp, rt.data_ptr(), rl.data_ptr())
+            he.he_sync(run.ctx)
+            bt.append(rt.cpu().numpy().copy())
+            bl.append(rl.cpu().numpy().copy())
+    a_t, a_l = toks.cpu().numpy(), lps.cpu().numpy()
+    run.close()
+    assert np.array_equal(a_t, np.stack(bt, axis=1))
+    assert np.array_equal(a_l.view(np.uint32), np.stack(bl, axis=1).view(np.uint32))
+
+
+def test_sample_batch_one(head_only):
+    wl, params = head_only
+    V = wl.actor.vocab
+    x = synth.sample_logits(1, V, seed=99)
+    run = GpuRun(wl, params)
+    d_x = x.cuda()
+    tok = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    lp = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(run.stream):
+        he.he_retake_cache(run.ctx, 1, 16)
+        he.he_sample(run.ctx, d_x.data_ptr(), 1, 40, he.he_sampling(0.9, 5, 0.8), tok.data_ptr(), lp.data_ptr())
+        he.he_sync(run.ctx)
+    want_t, want_lp, ok = _robust(x.numpy().astype(np.float64), 0.9, 5, np.arange(1), 40, 0.8)
+    run.close()
+    assert ok[0] and tok.item() == want_t[0] and abs(lp.item() - want_lp[0]) <= LP_TOL * max(1.0, abs(want_lp[0]))

@@ -142,3 +142,27 @@ def test_head_128_two_window_attention():
     om = O.OracleModel(shape, params, precision(shape), lora=lora, lora_scale=wl.lora_scale)
     want = SC.teacher_forced_logprobs(om, seq.numpy(), S_p)
     _compare(got, want, BF16_LP_TOL, "head 128, S = 400")
+
+
+def test_opt125m_scoring_batch_one_and_fp8_mode(c2):
+    """B = 1 with a one-token prompt and a two-token answer against the oracle; and the
+    scoring pass (a prompt pass: bf16 weights) is bit-for-bit the same whether or not
+    FP8 decode weights are switched on."""
+    params, lora = c2
+    seq = _experience(C2, C2.prompt_len, C2.gen_len)
+    run = GpuRun(C2, params)
+    got1 = _gpu_logprobs(run, seq[:1, :3], 1, lora_cpu=lora)
+    om = O.OracleModel(C2.actor, params, precision(C2.actor), lora=lora, lora_scale=C2.lora_scale)
+    _compare(got1, SC.teacher_forced_logprobs(om, seq.numpy()[:1, :3], 1), BF16_LP_TOL, "opt125m B=1 S=3")
+    B, S, S_p = C2.batch, 300, 200
+    ids = seq[:, :S].to(torch.int32).cuda()
+    outs = []
+    for f8 in (False, True):
+        out = torch.empty(B, S - S_p, dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(run.stream):
+            he.he_set_fp8_decode(run.ctx, f8)
+            he.he_logprobs(run.ctx, ids.data_ptr(), B, S, S_p, out.data_ptr())
+            he.he_sync(run.ctx)
+        outs.append(out.cpu().numpy())
+    run.close()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
