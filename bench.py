@@ -225,20 +225,33 @@ def main():
                          "the per-class traffic summary (no GPU)")
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --stats kernel_stats.csv into a markdown summary (no GPU)")
-    ap.add_argument("--command", default="", help="the command that produced the csv (recorded)")
+    ap.add_argument("--command", default="", help="the command that produced the csv (recorded; "
+                    "default: the standard profiling command for the summary being written)")
     args = ap.parse_args()
 
     if args.counters_summary:
         f, w, o = args.counters_summary
-        summ = counters_summary(f, w, args.workload, args.command)
+        cmd = args.command or (
+            f"export TMPDIR=/tmp && "
+            f"timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- "
+            f"python3 bench.py --workload {args.workload} --trace-steps 3 && "
+            f"timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- "
+            f"python3 bench.py --workload {args.workload} --trace-steps 3 && "
+            f"python3 bench.py --workload {args.workload} --counters-summary {f} {w} {o}")
+        summ = counters_summary(f, w, args.workload, cmd)
         with open(o, "w") as fh:
             json.dump(summ, fh, indent=1)
         print(json.dumps(summ["classes"], indent=1))
         return
     if args.stats_summary:
         st_csv, o = args.stats_summary
+        cmd = args.command or (
+            f"export TMPDIR=/tmp && "
+            f"timeout -k 10 400 rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof -o bench -- "
+            f"python3 bench.py --workload {args.workload} --steps 1 --warmup 1 --no-cpu --no-breakdown && "
+            f"python3 bench.py --workload {args.workload} --stats-summary {st_csv} {o}")
         with open(o, "w") as fh:
-            fh.write(stats_summary(st_csv, args.workload, args.command))
+            fh.write(stats_summary(st_csv, args.workload, cmd))
         return
 
     if args.gpus != 1:
