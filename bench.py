@@ -135,7 +135,10 @@ KERNEL_SOURCES = ["transformer_decode_amd/csrc/k_gemv.hip", "transformer_decode_
 def kernel_class(name):
     """The bench's kernel classes, from a kernel's demangled name."""
     if "gemv_il_kernel" in name or "gemv_f32_kernel" in name:
-        return "lmhead" if (name.rstrip(")").split(">")[0].endswith(", 2") or "ARGMAX" in name) else "gemv_decode"
+        # gemv_il_kernel<MT, FR, NWK, OUT, F8>: OUT 2 is the LM head's pick epilogue
+        targs = name.split("<", 1)[1].split(">", 1)[0].split(",") if "<" in name else []
+        mode = targs[3].strip() if "gemv_il_kernel" in name and len(targs) > 3 else targs[0].strip() if targs else ""
+        return "lmhead" if mode in ("2", "GV_ARGMAX") or "ARGMAX" in name else "gemv_decode"
     if "attn_decode_kernel" in name:
         return "attn_decode"
     if "gemm_" in name:
