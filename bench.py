@@ -188,6 +188,39 @@ def counters_summary(fetch_csv, write_csv, workload, command):
     return out
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def mfma_summary(csv_path, workload, command):
+    """Per-kernel MFMA work from one rocprofv3 --pmc pass of MFMA_COUNTERS: bf16 MFMA
+    flops = MOPS x 512 (to set beside the algorithmic 2 M N K), and the raw ratio of
+    MFMA busy cycles to GPU active cycles as the counters report them."""
+    import csv
+    disp = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = disp.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    per = {}
+    for d in disp.values():
+        if not all(c in d for c in MFMA_COUNTERS) or d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] <= 0:
+            continue
+        e = per.setdefault(d["name"], [0, 0.0, 0.0, 0.0])
+        e[0] += 1
+        e[1] += d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        e[2] += d["SQ_VALU_MFMA_BUSY_CYCLES"]
+        e[3] += d["GRBM_GUI_ACTIVE"] * 256 * 4
+    lines = [f"# MFMA work and utilisation, {workload}", "", "Command (run from the repository root, output under "
+             "gpurun_out/):", "", "```", command, "```", "",
+             "bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per dispatch. busy / active = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE summed over the kernel's dispatches, as the counters "
+             "report them (their normalisation over XCDs, CUs and SIMDs is not restated here; the rate against "
+             "peak comes from kernel time).", "",
+             "| kernel | dispatches | MFMA TFLOP per dispatch | MFMA busy / GPU active |", "|---|---|---|---|"]
+    for name, (n, fl, busy, act) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| `{name[:100]}` | {n} | {fl / n / 1e12:.3f} | {busy / (act / 1024):.1f} |")
+    return "\n".join(lines) + "\n"
+
+
 def stats_summary(stats_csv, workload, command):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
@@ -228,6 +261,8 @@ def main():
                          "the per-class traffic summary (no GPU)")
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --stats kernel_stats.csv into a markdown summary (no GPU)")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("MFMA_CSV", "OUT_MD"),
+                    help="turn a rocprofv3 --pmc pass of the MFMA counters into a markdown summary (no GPU)")
     ap.add_argument("--command", default="", help="the command that produced the csv (recorded; "
                     "default: the standard profiling command for the summary being written)")
     args = ap.parse_args()
@@ -245,6 +280,16 @@ def main():
         with open(o, "w") as fh:
             json.dump(summ, fh, indent=1)
         print(json.dumps(summ["classes"], indent=1))
+        return
+    if args.mfma_summary:
+        m_csv, o = args.mfma_summary
+        cmd = args.command or (
+            f"export TMPDIR=/tmp && "
+            f"timeout -s KILL 120 rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d gpurun_out/pmc_mfma -o mfma -- "
+            f"python3 bench.py --workload {args.workload} --trace-steps 3 && "
+            f"python3 bench.py --workload {args.workload} --mfma-summary {m_csv} {o}")
+        with open(o, "w") as fh:
+            fh.write(mfma_summary(m_csv, args.workload, cmd))
         return
     if args.stats_summary:
         st_csv, o = args.stats_summary
