@@ -651,7 +651,10 @@ he_status he_release_cache(he_ctx* c) {
 he_status he_destroy(he_ctx* c) {
   if (!c) return HE_OK;
   he_status s = he_release_cache(c);
-  if (c->f8buf) hipFree(c->f8buf);
+  if (c->f8buf) {
+    if (!c->validate_only) (void)hipStreamSynchronize(c->stream);   // no kernel still reads the copy
+    hipFree(c->f8buf);
+  }
   if (!c->validate_only) {
     for (Timer& t : c->timers) {
       for (auto& p : t.live) { hipEventDestroy(p.first); hipEventDestroy(p.second); }
