@@ -615,6 +615,50 @@ def main():
         res["phases"]["graph_speedup"] = t_dec_direct / (res["phases"]["decode_ms"] / 1e3)
         log(f"decode without graph: {t_dec_direct * 1e3:.1f} ms (graph gain x{res['phases']['graph_speedup']:.3f})")
 
+    if not args.no_breakdown:
+        # reward scoring (the largest workload's OPT-350m-shape reward model, post-LN, its own
+        # shape): 128 sequences x 512 tokens, one full causal pass plus the scalar head
+        rw = synth.WORKLOADS["opt13b"]
+        rs = rw.reward
+        RB, RS = rw.batch, rw.max_seq
+        rdev = {k: v.cuda() for k, v in synth.model_params(rs, args.seed).items()}
+        rids = synth.tokens(args.seed, "reward_ids", (RB, RS), rs.vocab).cuda()
+        reward = torch.empty(RB, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        eng3 = he.Engine(rs, rdev)
+        with torch.cuda.stream(eng3.stream):
+            he.he_retake_cache(eng3.ctx, RB, RS)
+            he.he_score(eng3.ctx, rids.data_ptr(), RB, RS, reward.data_ptr())      # warm-up
+            E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            E[0].record(eng3.stream)
+            for _ in range(3):
+                he.he_score(eng3.ctx, rids.data_ptr(), RB, RS, reward.data_ptr())
+            E[1].record(eng3.stream)
+            rcls = {"gemm": he.HE_K_GEMM_PREFILL, "attn": he.HE_K_ATTN_PREFILL, "norm": he.HE_K_EMBED_NORM,
+                    "head": he.HE_K_SCORE}
+            for k in rcls.values():
+                he.he_kernel_timer(eng3.ctx, k, True)
+            he.he_score(eng3.ctx, rids.data_ptr(), RB, RS, reward.data_ptr())
+            rst = {n: he.he_kernel_stats(eng3.ctx, k) for n, k in rcls.items()}
+            for k in rcls.values():
+                he.he_kernel_timer(eng3.ctx, k, False)
+            he.he_release_cache(eng3.ctx)
+            he.he_sync(eng3.ctx)
+            torch.cuda.synchronize()
+        eng3.close()
+        t_rm = E[0].elapsed_time(E[1]) / 1e3 / 3
+        de, dr, Lr, Fr = rs.embed_dim, rs.d_model, rs.n_layers, rs.d_ffn
+        rm_flops = (2.0 * RB * RS * (Lr * (4 * dr * dr + 2 * dr * Fr) + de * dr)   # layers + project_in
+                    + 2.0 * Lr * dr * RS * (RS + 1) * RB + 2.0 * RB * dr * de)
+        res["reward_scoring"] = {
+            "model": "opt-350m shape (post-LN, d 1024, 24 layers, embedding 512)", "batch": RB, "seq_len": RS,
+            "ms": t_rm * 1e3, "sequences_per_s": RB / t_rm, "tokens_per_s": RB * RS / t_rm,
+            "TFLOPs": rm_flops / t_rm / 1e12, "mfma_frac": rm_flops / t_rm / BF16_PEAK,
+            "rewards_finite": bool(torch.isfinite(reward).all().item()),
+            "class_ms": {n: v.total_ms for n, v in rst.items()},
+            "gemm_TFLOPs": rst["gemm"].flops / (rst["gemm"].total_ms / 1e3) / 1e12 if rst["gemm"].total_ms else None}
+        log(f"reward_scoring: {json.dumps(res['reward_scoring'])}")
+
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.seed)
