@@ -329,20 +329,18 @@ __global__ __launch_bounds__(512) void gemm_bf16_big_kernel(const bf16* __restri
 
 // ---------------------------------------------------------------------------------
 // bf16 MFMA GEMM on 32 x 32 x 16 tiles staged by LDS DMA (M, N multiples of 256,
-// K of 32).  256 x 256 macro tile, 4 waves (2 x 2), each owning 128 x 128 as 4 x 4
-// v_mfma_f32_32x32x16_bf16 tiles (accumulators in AGPRs).  With one wave per SIMD
-// this instruction sustains about 2.1 PFLOP/s on constant operands (1.65 to 1.7 on
-// random ones, where power sets the clock) where the 16 x 16 x 32 one stops near 1.3
-// (measured).  An operand fragment is 32 rows x 16 k = 1 KB, lane l holding row
-// l % 32, k 8 (l / 32) .. + 8.  A stage is 32 k, staged as 16 fragments of X and 16
-// of W in the 16 x 32 shape of the weights' inference layout (1 KB each, lane l at
-// row l % 16, k 8 (l / 16)), filled with buffer_load_dwordx4 ... lds: each lane's 16
-// bytes (8 consecutive k of one row) land at slot + 16 l.  A W fragment in the
-// inference layout is 1 KB of consecutive bytes (whole cache lines); row-major X is
-// 16 rows x 64 bytes.  The 32 x 32 x 16 operands are read back from pairs of
-// fragments with ds_read_b128 free of bank conflicts, and never pass through VGPRs
-// on the way in.  Four stages (128 KB of LDS) rotate: loads run three stages ahead
-// of the MFMAs.
+// K of 32).  256 x 256 macro tile.  The 32 x 32 x 16 instruction sustains about
+// 2.1 PFLOP/s on constant operands (1.65 to 1.7 on random ones, where power sets the
+// clock) where the 16 x 16 x 32 one stops near 1.3 with one wave per SIMD (measured).
+// An operand fragment is 32 rows x 16 k = 1 KB, lane l holding row l % 32, k 8 (l / 32)
+// .. + 8.  A stage is 32 k, staged as 16 fragments of X and 16 of W in the 16 x 32
+// shape of the weights' inference layout (1 KB each, lane l at row l % 16, k 8 (l / 16)),
+// filled with buffer_load_dwordx4 ... lds: each lane's 16 bytes (8 consecutive k of one
+// row) land at slot + 16 l.  A W fragment in the inference layout is 1 KB of
+// consecutive bytes (whole cache lines); row-major X is 16 rows x 64 bytes.  The
+// 32 x 32 x 16 operands are read back from pairs of fragments with ds_read_b128 free of
+// bank conflicts, and never pass through VGPRs on the way in.  Four stages (128 KB of
+// LDS) rotate: loads run three stages ahead of the MFMAs.
 // ---------------------------------------------------------------------------------
 constexpr int FBM = 256, FBN = 256, FST = 4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -388,17 +386,21 @@ __device__ __forceinline__ uint32_t frag_step_part(int s, int K, int il) {
   return (uint32_t)(((q << 6) >> (il - 3)) * K + ((s >> (il - 5)) << il));
 }
 
+// Eight waves (2 x 4), each owning 128 x 64 of the macro tile as 4 x 2 32 x 32 tiles:
+// 128 accumulator registers per wave, so two waves share each SIMD and one issues MFMAs
+// while the other waits at the stage barrier or for its LDS reads (measured 3 to 4%
+// faster than four waves of 128 x 128 with one wave per SIMD on the 6.7B prompt-pass
+// shapes, 11% on K = 1024 shapes).  Each wave loads two X and two W fragments per stage;
+// per 16-wide k-step it reads 2 W and 4 X operands for 8 MFMAs.
 template <int MODE, bool WIL, bool XIL>
-__global__ __launch_bounds__(256) void gemm_frag_kernel(const bf16* __restrict__ X,
-                                                        const bf16* __restrict__ W, int M, int N,
-                                                        int K, EpiArgs e) {
-  // [stage][operand][fragment f = ks * 8 + row tile][512 elements]
+__global__ __launch_bounds__(512) void gemm_frag_kernel(const bf16* __restrict__ X,
+                                                         const bf16* __restrict__ W, int M, int N,
+                                                         int K, EpiArgs e) {
   __shared__ __attribute__((aligned(1024))) bf16 fsm[FST * 2 * 16 * 512];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 2, wn = wv & 3;
 
-  // XCD-aware tile order (WG w runs on XCD w % 8), groups of 4 tile rows
   const int nm = M / FBM, nn = N / FBN, T = nm * nn;
   const int per = (T + 7) / 8;
   const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -408,29 +410,22 @@ __global__ __launch_bounds__(256) void gemm_frag_kernel(const bf16* __restrict__
   const int gsz = min(nm - first_m, GM);
   const int tm = first_m + (t % (GM * nn)) % gsz, tn = (t % (GM * nn)) / gsz;
   const int m0 = tm * FBM, n0 = tn * FBN;
-  // Stage s (k 32 s .. + 32) holds each operand as 16 fragments of 16 rows x 32 k
-  // (1 KB, lane l at row l % 16, k 8 (l / 16) .. + 8); this wave loads fragments
-  // 4 wv .. 4 wv + 3 of each.
   const int ilx = XIL ? e.x_il : 0, ilw = WIL ? e.w_il : 0;
-  // One buffer resource per operand over this tile's 256 rows (byte offsets within a
-  // tile stay far below 2^32: 256 K 2 bytes).
   const uint32_t tile_bytes = (uint32_t)(FBM * K * 2);
   const __amdgpu_buffer_rsrc_t rx = buf_rsrc(X + (size_t)m0 * K, tile_bytes);
   const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W + (size_t)n0 * K, tile_bytes);
-  // Byte offsets: per lane (lane part plus the row offset of each of this wave's four
-  // 16-row tiles, fixed for the kernel) and per stage (one scalar per operand).
+  // this wave's DMA: 16-row fragments 2 wv and 2 wv + 1 of each operand
   const uint32_t lane_x = frag_lane_part(lane, K, ilx), lane_w = frag_lane_part(lane, K, ilw);
-  uint32_t vx[4], vw[4];
+  uint32_t vx[2], vw[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t rows = (uint32_t)((wv * 4 + q) * 16 * K);
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t rows = (uint32_t)((wv * 2 + q) * 16 * K);
     vx[q] = (lane_x + rows) * 2;
     vw[q] = (lane_w + rows) * 2;
   }
-  // DMA g (0..7) of k-step s into stage buffer buf: 16-row tile 4 wv + g / 2 of X
-  // (g even) or W (g odd)
+  // DMA g (0..3): fragment 2 wv + g / 2 of X (g even) or W (g odd)
   auto dma = [&](int g, int s, int buf) {
-    bf16* sa = fsm + (size_t)buf * 2 * 16 * 512 + (wv * 4 + (g >> 1)) * 512;
+    bf16* sa = fsm + (size_t)buf * 2 * 16 * 512 + (wv * 2 + (g >> 1)) * 512;
     if ((g & 1) == 0)
       buf_dma16(rx, sa, vx[g >> 1], frag_step_part(s, K, ilx) * 2);
     else
@@ -438,117 +433,112 @@ __global__ __launch_bounds__(256) void gemm_frag_kernel(const bf16* __restrict__
   };
   auto issue = [&](int s, int buf) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) dma(g, s, buf);
+    for (int g = 0; g < 4; ++g) dma(g, s, buf);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Operands of one 16-wide k-step ks of a stage: b[0..3] then a[0..3] (wave tile
-  // columns, rows).  The 32 x 32 x 16 operand (lane l: row l % 32, k 8 (l / 32) .. + 8
+  // operand g of k-step ks of stage s: g < 2 column tile 2 wn + g of W, else row tile
+  // 4 wm + g - 2 of X.  The 32 x 32 x 16 operand (lane l: row l % 32, k 8 (l / 32) .. + 8
   // of the step) of 32-row tile t is gathered from the 16-row fragments 2t and 2t + 1:
-  // row r sits in fragment 2t + r / 16 at lane (r mod 16) + 16 (2 ks + l / 32).  Each
-  // 16 lanes read 256 consecutive bytes, so the reads are free of bank conflicts.
+  // row r sits in fragment 2t + r / 16 at lane (r mod 16) + 16 (2 ks + l / 32), so each
+  // 16 lanes read 256 consecutive bytes, free of bank conflicts.
   const int rl = lane & 31;
   const uint32_t lane_lds = (uint32_t)((rl >> 4) * 512 + ((rl & 15) + ((lane >> 5) << 4)) * 8);
-  // operand g of k-step ks of stage s: g < 4 column tile g of W, else row tile g - 4 of X
   auto read_frag = [&](int s, int ks, int g) -> bf16x8 {
     const bf16* sa = fsm + (size_t)(s & (FST - 1)) * 2 * 16 * 512 + ks * 256 + lane_lds;
-    return g < 4 ? *reinterpret_cast<const bf16x8*>(sa + 16 * 512 + (wn * 4 + g) * 1024)
-                 : *reinterpret_cast<const bf16x8*>(sa + (wm * 4 + g - 4) * 1024);
+    return g < 2 ? *reinterpret_cast<const bf16x8*>(sa + 16 * 512 + (wn * 2 + g) * 1024)
+                 : *reinterpret_cast<const bf16x8*>(sa + (wm * 4 + g - 2) * 1024);
   };
-  auto read_frags = [&](int s, int ks, bf16x8 (&r)[8]) {
-#pragma unroll
-    for (int g = 0; g < 8; ++g) r[g] = read_frag(s, ks, g);
+  // group g of a half-stage: MFMAs of row tile g with column tiles 0 and 1
+  auto mma2 = [&](const bf16x8 (&r)[6], int g) {
+    acc[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[0], r[2 + g], acc[g][0], 0, 0, 0);
+    acc[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[1], r[2 + g], acc[g][1], 0, 0, 0);
   };
-  auto mma = [&](const bf16x8 (&r)[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[j], r[4 + i], acc[i][j], 0, 0, 0);
+  // reads of group g: operands g (g < 2), then 2 and 3 (g = 2), 4 and 5 (g = 3)
+  auto reads = [&](bf16x8 (&r)[6], int s, int ks, int g) {
+    if (g < 2) {
+      r[g] = read_frag(s, ks, g);
+    } else {
+      r[2 * g - 2] = read_frag(s, ks, 2 * g - 2);
+      r[2 * g - 1] = read_frag(s, ks, 2 * g - 1);
+    }
   };
 
-  // With one wave per SIMD, instructions issue in order: the DMA issues and the LDS
-  // reads of the next k-step are spread between the MFMAs (scheduling groups) rather
-  // than queued in front of them.  r0 holds the first 16-wide k-step of a stage, r1
-  // the second; each is read one half-stage before its MFMAs.  The loop body is
-  // straight-line so the accumulators stay in place: every iteration issues one
-  // stage of DMA (the last FST - 1 repeat the final stage's addresses into the free
-  // buffer, which is never read again) and the last stage re-reads its own first
-  // k-step instead of a next one.
+  // The loop body is straight-line so the accumulators stay in place.  Each half-stage
+  // is four groups of one DMA issue, one or two LDS reads and two MFMAs, in that order,
+  // so the DMA issues and the reads of the next k-step are spread between the MFMAs
+  // rather than queued in front of them.  r0 holds the first 16-wide k-step of a stage,
+  // r1 the second; each is read one half-stage before its MFMAs.  Every iteration issues
+  // one stage of DMA (the last FST - 1 repeat the final stage's addresses into the free
+  // buffer, never read again) and the last stage re-reads its own first k-step.
   const int ns = K / 32;
 #pragma unroll
   for (int s = 0; s < FST - 1; ++s) issue(min(s, ns - 1), s);
-  HE_WAIT_VMCNT(8 * (FST - 2));
+  HE_WAIT_VMCNT(4 * (FST - 2));
   barrier_keep_loads();
-  bf16x8 r0[8], r1[8];
-  read_frags(0, 0, r0);
-  // group g of a half-stage: MFMAs (row tile g / 2, column tiles 2 (g % 2) + 0, 1)
-  auto mma2 = [&](const bf16x8 (&r)[8], int g) {
-    const int i = g >> 1, j = (g & 1) << 1;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[j], r[4 + i], acc[i][j], 0, 0, 0);
-    acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[j + 1], r[4 + i], acc[i][j + 1], 0, 0, 0);
-  };
+  bf16x8 r0[6], r1[6];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) reads(r0, 0, 0, g);
   for (int s = 0; s < ns; ++s) {
-    // half A: refill the buffer that stage s - 1 used (every wave read it before the
-    // last barrier), read the second k-step of stage s, multiply the first; each group
-    // is one DMA issue, one LDS read and two MFMAs, in that order
+    // half A: refill the buffer stage s - 1 used (every wave read it before the last
+    // barrier), read the second k-step of stage s, multiply the first
     const int sd = min(s + FST - 1, ns - 1), bd = (s + FST - 1) & (FST - 1);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int g = 0; g < 4; ++g) {
       dma(g, sd, bd);
-      r1[g] = read_frag(s, 1, g);
+      reads(r1, s, 1, g);
       mma2(r0, g);
       __builtin_amdgcn_sched_barrier(0);
     }
     // stage s + 1 must have landed here and in every wave before it is read
-    HE_WAIT_VMCNT(8 * (FST - 2));
+    HE_WAIT_VMCNT(4 * (FST - 2));
     barrier_keep_loads();
     // half B: read the first k-step of stage s + 1, multiply the second of stage s
     const int sn = s + 1 < ns ? s + 1 : s;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      r0[g] = read_frag(sn, 0, g);
+    for (int g = 0; g < 4; ++g) {
+      reads(r0, sn, 0, g);
       mma2(r1, g);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  HE_WAIT_VMCNT(0);     // the repeated tail stages land before LDS is reused below
+  HE_WAIT_VMCNT(0);
   barrier_keep_loads();
 
-  // Epilogue through LDS (free after the last barrier), a quarter of the wave tile at
-  // a time: the MFMAs compute W X^T per tile, so lane l holds output row l % 32 and
-  // register 4 q + c holds column 8 q + 4 (l / 32) + c; each wave parks 32 rows x 128
-  // columns (fp32, rows padded to 132 words: conflict-free 16-byte writes) in its own
-  // region, then reads them back as 8 consecutive columns per lane, so 16 lanes cover
-  // a row and every store is a 16- or 32-byte access to whole row segments.
-  constexpr int PR = 132;
+  // Epilogue through LDS (free after the last barrier), one 32-row tile at a time: the
+  // MFMAs compute W X^T per tile, so lane l holds output row l % 32 and register 4 q + c
+  // holds column 8 q + 4 (l / 32) + c; each wave parks 32 rows x 64 columns (fp32, rows
+  // padded to 68 words: conflict-free 16-byte writes) in its own region, then reads them
+  // back as 8 consecutive columns per lane, so 8 lanes cover a row and every store is a
+  // 16- or 32-byte access to whole row segments.
+  constexpr int PR = 68;
   float* park = reinterpret_cast<float*>(fsm) + (size_t)wv * 32 * PR;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4*>(park + rl * PR + j * 32 + q * 8 + ((lane >> 5) << 2)) =
             f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-    __builtin_amdgcn_s_waitcnt(0);   // lgkmcnt(0): this wave's parked rows are in LDS
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int seg = lane + it * 64, row = seg >> 4, col = (seg & 15) << 3;
+    for (int it = 0; it < 4; ++it) {
+      const int seg = lane + it * 64, row = seg >> 3, col = (seg & 7) << 3;
       float v[8];
       const float4 v0 = *reinterpret_cast<const float4*>(park + row * PR + col);
       const float4 v1 = *reinterpret_cast<const float4*>(park + row * PR + col + 4);
       v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-      epi_store8<MODE>(e, m0 + wm * 128 + i * 32 + row, n0 + wn * 128 + col, N, v);
+      epi_store8<MODE>(e, m0 + wm * 128 + i * 32 + row, n0 + wn * 64 + col, N, v);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // reads done before the next quarter overwrites
+    __builtin_amdgcn_s_waitcnt(0);
   }
 }
 
@@ -599,13 +589,13 @@ static void gemm_dispatch(int dt, const void* X, const void* W, int M, int N, in
       const int blocks = ((M / FBM) * (N / FBN) + 7) / 8 * 8;
       const bf16 *x = (const bf16*)X, *w = (const bf16*)W;
       if (e.w_il && e.x_il)
-        gemm_frag_kernel<MODE, true, true><<<blocks, 256, 0, st>>>(x, w, M, N, K, e);
+        gemm_frag_kernel<MODE, true, true><<<blocks, 512, 0, st>>>(x, w, M, N, K, e);
       else if (e.w_il)
-        gemm_frag_kernel<MODE, true, false><<<blocks, 256, 0, st>>>(x, w, M, N, K, e);
+        gemm_frag_kernel<MODE, true, false><<<blocks, 512, 0, st>>>(x, w, M, N, K, e);
       else if (e.x_il)
-        gemm_frag_kernel<MODE, false, true><<<blocks, 256, 0, st>>>(x, w, M, N, K, e);
+        gemm_frag_kernel<MODE, false, true><<<blocks, 512, 0, st>>>(x, w, M, N, K, e);
       else
-        gemm_frag_kernel<MODE, false, false><<<blocks, 256, 0, st>>>(x, w, M, N, K, e);
+        gemm_frag_kernel<MODE, false, false><<<blocks, 512, 0, st>>>(x, w, M, N, K, e);
       return;
     }
     const long big_tiles = (long)((M + LBM - 1) / LBM) * ((N + LBN - 1) / LBN);
