@@ -264,6 +264,14 @@ def test_fp8_decode_switch():
     he.he_set_fp8_decode(ctx, False)
     assert _status(he.he_fp8_export, ctx, 0, 0, P, P) == he.HE_E_STATE
     e.close()
+    # a refused switch changes nothing: the prompt pass still stands for a decode step
+    tiny = synth.WORKLOADS["tiny"].actor
+    e = he.Engine(tiny, _fake_params(tiny), validate_only=True)
+    he.he_retake_cache(e.ctx, 2, 32)
+    he.he_prefill(e.ctx, P, 2, 16, P)
+    assert _status(he.he_set_fp8_decode, e.ctx, True) == he.HE_E_UNSUPPORTED
+    he.he_decode_step(e.ctx, P, P, 0)
+    e.close()
     for bad in (synth.WORKLOADS["tiny"].actor,                                          # fp32
                 dataclasses.replace(shape, d_model=640, n_heads=10),                     # d % 256
                 dataclasses.replace(shape, d_ffn=2944),                                  # d_ffn % 256

@@ -683,8 +683,8 @@ static he_status f8_requantize(he_ctx* c) {
 he_status he_set_fp8_decode(he_ctx* c, int32_t enable) {
   if (!c) return HE_E_ARG;
   if (c->failed) return set_err(c, HE_E_HIP, "context failed earlier: %s", c->err.c_str());
-  c->prefilled = false;   // decode plans depend on the weight format: a new prompt pass
   if (!enable) {
+    c->prefilled = false;   // decode plans depend on the weight format: a new prompt pass
     if (c->f8buf && !c->validate_only) {
       HIP_TRY(c, hipStreamSynchronize(c->stream));
       hipFree(c->f8buf);
@@ -699,6 +699,7 @@ he_status he_set_fp8_decode(he_ctx* c, int32_t enable) {
   if (c->d % 256 || c->F % 256)
     return set_err(c, HE_E_UNSUPPORTED, "FP8 decode weights need d and d_ffn divisible by 256");
   if (c->f8_on) return f8_requantize(c);
+  c->prefilled = false;   // decode plans depend on the weight format: a new prompt pass
   const int d = c->d, F = c->F;
   const size_t nq[4] = {(size_t)3 * d * d, (size_t)d * d, (size_t)F * d, (size_t)d * F};
   const size_t ns[4] = {(size_t)3 * d, (size_t)d, (size_t)F, (size_t)d};
