@@ -1068,10 +1068,26 @@ static he_status generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t
   return HE_OK;
 }
 
+// The pick rule as it stood before a call that may be refused: a refused call
+// (argument or state error, nothing enqueued) puts it back.
+struct RuleKeep {
+  he_ctx* c;
+  float it, tp;
+  uint64_t seed;
+  bool lp;
+  explicit RuleKeep(he_ctx* c_) : c(c_), it(c_->inv_temp), tp(c_->top_p), seed(c_->seed), lp(c_->want_logp) {}
+  void restore() { c->inv_temp = it; c->top_p = tp; c->seed = seed; c->want_logp = lp; }
+  he_status done(he_status s) {
+    if (s != HE_OK && s != HE_E_HIP) restore();
+    return s;
+  }
+};
+
 he_status he_generate(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g, int32_t* d_out) {
   if (!c) return HE_E_ARG;
+  RuleKeep keep(c);
   set_greedy(c);
-  return generate(c, d_prompt, B, S, S_g, d_out, nullptr);
+  return keep.done(generate(c, d_prompt, B, S, S_g, d_out, nullptr));
 }
 
 // Pick rule from he_sampling (NULL: greedy) into the context; checked before use.
@@ -1096,9 +1112,10 @@ static he_status set_rule(he_ctx* c, const he_sampling* smp, bool want_logp) {
 he_status he_generate_ex(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t S, int32_t S_g,
                          const he_sampling* smp, int32_t* d_out, float* d_logprobs) {
   if (!c) return HE_E_ARG;
+  RuleKeep keep(c);
   he_status s = set_rule(c, smp, d_logprobs != nullptr);
-  if (s != HE_OK) return s;
-  return generate(c, d_prompt, B, S, S_g, d_out, d_logprobs);
+  if (s != HE_OK) return keep.done(s);
+  return keep.done(generate(c, d_prompt, B, S, S_g, d_out, d_logprobs));
 }
 
 he_status he_sample(he_ctx* c, const float* d_logits, int32_t B, int32_t position, const he_sampling* smp,
@@ -1111,14 +1128,12 @@ he_status he_sample(he_ctx* c, const float* d_logits, int32_t B, int32_t positio
   if (B < 1 || B > c->max_batch) return set_err(c, HE_E_ARG, "batch %d outside 1..%d", B, c->max_batch);
   if (position < 0) return set_err(c, HE_E_ARG, "position %d < 0", position);
   // the rule of this call only: the context's own (used by he_decode_step) is kept
-  const float keep_it = c->inv_temp, keep_tp = c->top_p;
-  const uint64_t keep_seed = c->seed;
-  const bool keep_lp = c->want_logp;
+  RuleKeep keep(c);
   s = set_rule(c, smp, d_logprobs != nullptr);
   const float it = c->inv_temp, tp = c->top_p;
   const uint64_t seed = c->seed;
   const bool want_lp = c->want_logp;
-  c->inv_temp = keep_it; c->top_p = keep_tp; c->seed = keep_seed; c->want_logp = keep_lp;
+  keep.restore();
   if (s != HE_OK) return s;
   if (c->validate_only) return HE_OK;
   hipStream_t st = c->stream;
