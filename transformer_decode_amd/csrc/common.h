@@ -105,6 +105,14 @@ __device__ __forceinline__ size_t xt_off(int m, int k, int mt) {
   return ((size_t)((k >> 5) * mt + (m >> 4)) << 9) + (((m & 15) | (((k >> 3) & 3) << 4)) << 3) + (k & 7);
 }
 
+// 16 bytes read once (a weight or KV stream): a non-temporal load, which does not keep
+// the line in the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_once(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // FP8 (E4M3) decode-weight layout of W [N][K] (N % 16 == 0, K % 64 == 0): blocks of
 // 16 rows x 64 k, 1 KB each, row block major then k, so a row block's whole K range
 // is contiguous.  Lane l of a block holds row l % 16 and, in its 16 bytes, k 8 (l / 16)

@@ -29,7 +29,7 @@ namespace he {
 template <typename T> struct Raw8;
 template <> struct Raw8<bf16> {
   uint4 u;
-  __device__ __forceinline__ void load(const bf16* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load(const bf16* p) { u = ld_once(p); }   // K / V read once
   __device__ __forceinline__ void unpack(float* o) const {
     o[0] = __uint_as_float(u.x << 16); o[1] = __uint_as_float(u.x & 0xffff0000u);
     o[2] = __uint_as_float(u.y << 16); o[3] = __uint_as_float(u.y & 0xffff0000u);
@@ -452,7 +452,7 @@ __device__ __forceinline__ void pf_stage(const bf16* __restrict__ kc, const bf16
   for (int i = tid; i < Wp * NCH; i += 512) {
     const int key = i / NCH, c = i - key * NCH;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (kw0 + key < S) v = *reinterpret_cast<const uint4*>(kc + head + (size_t)(kw0 + key) * D + c * 8);
+    if (kw0 + key < S) v = ld_once(kc + head + (size_t)(kw0 + key) * D + c * 8);
     *reinterpret_cast<uint4*>(&Ks[key * D + ((c ^ ((key / RPB) & (NCH - 1))) << 3)]) = v;
   }
   for (int i = tid; i < (Wp / 8) * NCH; i += 512) {
@@ -462,7 +462,7 @@ __device__ __forceinline__ void pf_stage(const bf16* __restrict__ kc, const bf16
     for (int r = 0; r < 8; ++r) {
       const int key = kw0 + kb * 8 + r;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < S) v = *reinterpret_cast<const uint4*>(vc + head + (size_t)key * D + c * 8);
+      if (key < S) v = ld_once(vc + head + (size_t)key * D + c * 8);
       e[r][0] = v.x; e[r][1] = v.y; e[r][2] = v.z; e[r][3] = v.w;
     }
 #pragma unroll
