@@ -511,10 +511,12 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
     r.mode = EPI_RESID; r.bias = w.b_out; r.h = c->h; r.w_il = ild; r.x_il = ald;
     run_k(c, HE_K_GEMM_PREFILL, (double)d * d * es, 2.0 * M * d * d,
           [&] { launch_gemm(dt, c->o, w.w_out, M, d, d, r, st); });
-    if (post)
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln1_g, w.ln1_b, eps, c->x, M, d, 1, 0, 1, -ald, st);
-    else
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, -ald, st);
+    run_k(c, HE_K_EMBED_NORM, (double)M * d * (4 + es + (post ? 4 : 0)), 0, [&] {
+      if (post)
+        launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln1_g, w.ln1_b, eps, c->x, M, d, 1, 0, 1, -ald, st);
+      else
+        launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 0, -ald, st);
+    });
     EpiArgs f1;
     f1.mode = EPI_RELU; f1.bias = w.b_fc1; f1.out = c->a; f1.w_il = ild; f1.x_il = ald; f1.o_il = alf;
     run_k(c, HE_K_GEMM_PREFILL, (double)F * d * es, 2.0 * M * F * d,
@@ -525,11 +527,15 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
           [&] { launch_gemm(dt, c->a, w.w_fc2, M, d, F, f2, st); });
     // post-LN: the last layer's output goes to the head, which reads x row-major
     if (post)
-      launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 1,
-                  l + 1 < c->L ? -ald : 0, st);
+      run_k(c, HE_K_EMBED_NORM, (double)M * d * (8 + es), 0, [&] {
+        launch_norm(dt, c->h, nullptr, 0, nullptr, w.ln2_g, w.ln2_b, eps, c->x, M, d, 1, 0, 1,
+                    l + 1 < c->L ? -ald : 0, st);
+      });
     else if (l + 1 < c->L)
-      launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[l + 1].ln1_g, c->layers[l + 1].ln1_b, eps, c->x,
-                  M, d, 1, 0, 0, -ald, st);
+      run_k(c, HE_K_EMBED_NORM, (double)M * d * (4 + es), 0, [&] {
+        launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[l + 1].ln1_g, c->layers[l + 1].ln1_b, eps,
+                    c->x, M, d, 1, 0, 0, -ald, st);
+      });
   }
   int xs = S;
   if (!post) {   // pre-LN: final LayerNorm of the last position

@@ -409,9 +409,91 @@ __global__ __launch_bounds__(1024) void norm_kernel(float* __restrict__ h,
   ln_write_pre<T>(v, gv, bv, d, eps, x, r, x_lay, post ? hr : nullptr, red);
 }
 
+// LayerNorm of many rows with no split-K sum to add (the prompt pass, scoring, the
+// reward model): one wave per row, lane l holding chunks of 4 at l, l + 64, ...  The
+// row's mean and variance are wave reductions, with no block barrier, so the four
+// waves of a WG and the WGs of a CU run their rows independently and keep HBM busy.
+template <typename T, int NC>
+__global__ __launch_bounds__(256, NC <= 16 ? 4 : 3) void norm_rows_kernel(float* __restrict__ h, const T* __restrict__ g,
+                                                        const T* __restrict__ b, float eps,
+                                                        T* __restrict__ x, int M, int d, int row_stride,
+                                                        int row_offset, int post, int x_lay,
+                                                        int row_group) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;
+  const size_t row = (size_t)(r / row_group) * row_stride + row_offset + r % row_group;
+  float* hr = h + row * d;
+  const int nch = d / 4;
+  float v[NC][4];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = lane + c * kWave;
+    if (ch < nch) ld4(hr + ch * 4, v[c]);
+    else v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.f;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += v[c][q];
+  const float mean = wave_sum(s) / (float)d;
+  float s2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (lane + c * kWave < nch)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { const float t = v[c][q] - mean; s2 += t * t; }
+  const float var = wave_sum(s2) / (float)d;
+  const float rstd = 1.f / sqrtf(var + eps);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = lane + c * kWave;
+    if (ch < nch) {
+      float gv[4], bv[4], y[4];
+      ld4(g + ch * 4, gv);
+      ld4(b + ch * 4, bv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = (v[c][q] - mean) * rstd * gv[q] + bv[q];
+      if (post) st4(hr + ch * 4, y);                // post-LN: the stream is the norm
+      st4(x_at(x, r, ch * 4, d, x_lay), y);         // GEMM input: rounded
+    }
+  }
+}
+
+template <typename T>
+static bool launch_norm_rows(float* h, const T* g, const T* b, float eps, T* x, int M, int d,
+                             int row_stride, int row_offset, int post, int x_lay, int row_group,
+                             hipStream_t st) {
+  const int per_lane = (d / 4 + kWave - 1) / kWave;
+  const dim3 grid((M + 3) / 4), block(256);
+#define HE_NORM_ROWS(NC)                                                                          \
+  norm_rows_kernel<T, NC><<<grid, block, 0, st>>>(h, g, b, eps, x, M, d, row_stride, row_offset, \
+                                                  post, x_lay, row_group)
+  if (per_lane <= 4) HE_NORM_ROWS(4);
+  else if (per_lane <= 8) HE_NORM_ROWS(8);
+  else if (per_lane <= 16) HE_NORM_ROWS(16);
+  else if (per_lane <= 20) HE_NORM_ROWS(20);
+  else return false;
+#undef HE_NORM_ROWS
+  return true;
+}
+
+// Rows at or above which a norm with no partials to sum takes one wave per row.
+constexpr int kNormRowsMin = 256;
+
 void launch_norm(int dt, float* h, const float* parts, int nsplit, const void* bias, const void* g,
                  const void* b, float eps, void* x, int M, int d, int row_stride, int row_offset,
                  int post, int x_lay, hipStream_t st, int row_group) {
+  if (!parts && M >= kNormRowsMin) {
+    const bool done =
+        dt == DT_BF16
+            ? launch_norm_rows<bf16>(h, (const bf16*)g, (const bf16*)b, eps, (bf16*)x, M, d, row_stride,
+                                     row_offset, post, x_lay, row_group, st)
+            : launch_norm_rows<float>(h, (const float*)g, (const float*)b, eps, (float*)x, M, d,
+                                      row_stride, row_offset, post, 0, row_group, st);
+    if (done) return;
+  }
   const int nt = ln_threads(d);
   if (dt == DT_BF16)
     norm_kernel<bf16><<<M, nt, 0, st>>>(h, parts, nsplit, (const bf16*)bias, (const bf16*)g,
