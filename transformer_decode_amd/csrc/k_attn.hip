@@ -431,14 +431,14 @@ __device__ __forceinline__ float sum32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 constexpr int kPfKV = 32768;           // bf16 elements of each of K and V^T in LDS
-// Key window held in LDS at once for head size D.
-constexpr int pf_window(int D) { return kPfKV / D; }
+// Key window held in LDS at once for head size D and KV elements of each array.
+constexpr int pf_window(int D, int KV = kPfKV) { return KV / D; }
 // Keys padded for the LDS layout when the head fits in one window (a multiple of 128,
 // at least 128); the full window when it takes two; 0 when it does not fit in two.
-static int pf_pad(int S, int D) {
+static int pf_pad(int S, int D, int KV = kPfKV) {
   const int sp = S <= 128 ? 128 : (S + 127) / 128 * 128;
-  if (sp * D <= kPfKV) return sp;
-  return S <= 2 * pf_window(D) ? pf_window(D) : 0;
+  if (sp * D <= KV) return sp;
+  return S <= 2 * pf_window(D, KV) ? pf_window(D, KV) : 0;
 }
 
 // Stage keys kw0 .. kw0 + Wp - 1 of one head (zeros past S) into the LDS arrays:
@@ -599,15 +599,15 @@ __device__ __forceinline__ void pf_store(PfBlock<D>& s, bf16* __restrict__ o, in
 // windows: blocks whose queries lie in the first window finish there; the blocks of
 // the second window (W / 128 per wave) run over the first window's keys, keep their
 // state in registers across the restaging barrier, and finish over the second's.
-template <int D>
-__global__ __launch_bounds__(512) void attn_prefill_lds_kernel(const bf16* __restrict__ q,
+template <int D, int KV = kPfKV>
+__global__ __launch_bounds__(512, KV < kPfKV ? 4 : 2) void attn_prefill_lds_kernel(const bf16* __restrict__ q,
                                                                const bf16* __restrict__ kc,
                                                                const bf16* __restrict__ vc,
                                                                bf16* __restrict__ o, int S, int S_pad,
                                                                int H, int S_max, int o_il) {
-  constexpr int W = pf_window(D), ND = W / 128;   // window; second-window blocks per wave
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kPfKV];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[kPfKV];
+  constexpr int W = pf_window(D, KV), ND = W / 128;   // window; second-window blocks per wave
+  __shared__ __attribute__((aligned(16))) bf16 Ks[KV];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[KV];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -706,16 +706,21 @@ __global__ __launch_bounds__(64) void attn_prefill_f32_kernel(const float* __res
 void launch_attn_prefill(int dt, const void* q, const void* k_cache, const void* v_cache, void* o,
                          int B, int S, int H, int D, int S_max, int o_il, hipStream_t st) {
   if (dt == DT_BF16 && (D == 32 || D == 64 || D == 128) && pf_pad(S, D)) {
-    const int sp = pf_pad(S, D);
-    if (D == 128)
-      attn_prefill_lds_kernel<128><<<B * H, 512, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
-                                                          (const bf16*)v_cache, (bf16*)o, S, sp, H, S_max, o_il);
-    else if (D == 64)
-      attn_prefill_lds_kernel<64><<<B * H, 512, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
-                                                         (const bf16*)v_cache, (bf16*)o, S, sp, H, S_max, o_il);
-    else
-      attn_prefill_lds_kernel<32><<<B * H, 512, 0, st>>>((const bf16*)q, (const bf16*)k_cache,
-                                                         (const bf16*)v_cache, (bf16*)o, S, sp, H, S_max, o_il);
+    // Heads whose keys fit in two windows of half the LDS take 64 KB per WG, so two WGs
+    // share a CU and one stages its head while the other computes.
+    const bool half = pf_pad(S, D, kPfKV / 2) != 0;
+    const int sp = half ? pf_pad(S, D, kPfKV / 2) : pf_pad(S, D);
+#define HE_PF(DD, KV)                                                                                 \
+  attn_prefill_lds_kernel<DD, KV><<<B * H, 512, 0, st>>>((const bf16*)q, (const bf16*)k_cache,        \
+                                                         (const bf16*)v_cache, (bf16*)o, S, sp, H, S_max, o_il)
+    if (D == 128) {
+      if (half) HE_PF(128, kPfKV / 2); else HE_PF(128, kPfKV);
+    } else if (D == 64) {
+      if (half) HE_PF(64, kPfKV / 2); else HE_PF(64, kPfKV);
+    } else {
+      if (half) HE_PF(32, kPfKV / 2); else HE_PF(32, kPfKV);
+    }
+#undef HE_PF
   } else if (dt == DT_BF16) {
     dim3 grid((S + 63) / 64, B * H);
     if (D == 64)
