@@ -77,8 +77,9 @@ GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole, 
   };
   if (whole) {   // one group, a K range of K / nwk per wave
     auto rows = [&](int fr) { return (long)(nrb + fr - 1) / fr; };
-    if (rows(frmax) >= 512) {         // enough single-wave WGs (the LM head)
-      p.fr = frmax; p.nwk = 1; p.kr = K; p.splits = 1;
+    if (rows(frmax) >= 512) {         // enough WGs (the LM head): two waves split K
+      const int kq = f8 ? 256 : 128;
+      p.fr = frmax; p.nwk = K % (2 * kq) == 0 ? 2 : 1; p.kr = K / p.nwk; p.splits = 1;
       return p;
     }
     // few row groups (QKV): fill the 256 CUs evenly -- the fewest rounds of 256 WGs
