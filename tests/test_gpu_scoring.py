@@ -95,6 +95,22 @@ def test_opt125m_logprobs_two_chunks(c2, fuse):
     _compare(got[rows], want, BF16_LP_TOL, f"opt125m fused={fuse}")
 
 
+def test_opt125m_logprobs_ragged_rows(c2):
+    """Three sequences of 301 tokens, S_p = 200: the prompt layers run on 903 rows and
+    the scored norm on 303 (row groups of 101). Both are above the size where the
+    LayerNorm takes one wave per row, and neither is a multiple of that kernel's four
+    rows per WG, so the last WG is partly empty. Every position is checked."""
+    params, lora = c2
+    S_p, S = 200, 301
+    seq = _experience(C2, C2.prompt_len, C2.gen_len)[:3, :S].contiguous()
+    run = GpuRun(C2, params)
+    got = _gpu_logprobs(run, seq, S_p, lora_cpu=lora)
+    run.close()
+    om = O.OracleModel(C2.actor, params, precision(C2.actor), lora=lora, lora_scale=C2.lora_scale)
+    want = SC.teacher_forced_logprobs(om, seq.numpy(), S_p)
+    _compare(got, want, BF16_LP_TOL, "opt125m 3 x 301 rows")
+
+
 def test_opt125m_scoring_reproduces_generation_logprobs(c2):
     """Sampling at T = 1 reports log softmax(logits) of each pick from the decode
     route; scoring the finished sequence recomputes them from the prompt-pass route.
