@@ -59,15 +59,31 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// Reductions over the 64 lanes of a wave (all lanes active), the same bits in every
+// lane: DPP moves within each row of 16 lanes (swap neighbours, swap pairs, mirror
+// within 8, mirror within 16), then the gfx950 lane swaps between rows 16 and 32
+// apart.  Each step combines two values with a commutative operation, so partner lanes
+// compute the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_move<0xB1>(v));     // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));     // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));    // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));    // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // ---------------------------------------------------------------------------------
