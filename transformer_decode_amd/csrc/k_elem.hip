@@ -429,8 +429,13 @@ __global__ __launch_bounds__(256, NC <= 16 ? 4 : 3) void norm_rows_kernel(float*
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int ch = lane + c * kWave;
-    if (ch < nch) ld4(hr + ch * 4, v[c]);
-    else v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.f;
+    if (ch < nch) {                              // the stream row is read once here
+      const uint4 u = ld_once(hr + ch * 4);
+      v[c][0] = __uint_as_float(u.x); v[c][1] = __uint_as_float(u.y);
+      v[c][2] = __uint_as_float(u.z); v[c][3] = __uint_as_float(u.w);
+    } else {
+      v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.f;
+    }
   }
   float s = 0.f;
 #pragma unroll
