@@ -51,76 +51,76 @@ def algorithmic(wl):
     return dec_bytes, dec_flops, pre_flops, step_w
 
 
-def cpu_baseline(wl, seed=0, layers=2, rows=(0, 1, 32, 63), steps=4):
-    """The CPU oracle on a bounded sample of the workload, extrapolated to a full row set.
-
-    Sample: the rows `rows`, the first `layers` decoder layers (LoRA fold of those
-    layers, prompt pass of 256 tokens, `steps` cached decode steps) plus the final
-    LayerNorm and LM head.  Every layer has the same shape, so the per-layer time
-    scales to all layers; decode steps scale to 255 (the per-step cost grows with
-    the context, which the sample's steps, taken at the start, understate slightly).
-    """
-    import dataclasses
-
+def cpu_baseline(wl, seed=0):
+    """The CPU oracle timed on the sampled rows {0, 1, B/2, B-1} of the workload, whole:
+    the LoRA fold of every layer, the prompt pass of those rows and all gen_len - 1
+    cached decode steps (greedy, the oracle's own picks), every layer; then one decode
+    step of the full batch (its KV cache holds prompt_len positions of synthetic
+    contents, since only the step's cost is wanted).  Nothing is extrapolated: the rate
+    is the sampled rows' generated tokens over the measured time."""
     import numpy as np
-    import torch
 
     import synth
     from oracle import opt_he as O
 
     a = wl.actor
-    rows = [r for r in rows if r < wl.batch]
-    sub = dataclasses.replace(a, n_layers=layers)
+    B = wl.batch
+    rows = sorted({0, 1, B // 2, B - 1})
     t0 = time.time()
-    params = synth.model_params(sub, seed)
-    lora = synth.lora_params(sub, wl.lora_rank, seed)
-    prompts = synth.prompts(wl, seed).numpy()[rows]
+    params = synth.model_params(a, seed)
+    lora = synth.lora_params(a, wl.lora_rank, seed)
+    prompts = synth.prompts(wl, seed).numpy()
     log(f"cpu baseline inputs ready in {time.time() - t0:.1f}s")
-    threads = torch.get_num_threads()
-    om = O.OracleModel(sub, params, O.Precision("bf16"), lora=lora, lora_scale=wl.lora_scale,
+    om = O.OracleModel(a, params, O.Precision("bf16"), lora=lora, lora_scale=wl.lora_scale,
                        cache_layers=True)
     t = time.time()
-    for i in range(layers):
-        om.layer(i)                         # LoRA fold (and widening) of the sampled layers
+    for i in range(a.n_layers):
+        om.layer(i)                         # LoRA fold (and widening) of every layer
     t_fold = time.time() - t
+    log(f"cpu baseline: fold {t_fold:.1f}s")
     t = time.time()
-    lg, cache = om.prefill(prompts, wl.max_seq)
+    lg, cache = om.prefill(prompts[rows], wl.max_seq)
     t_prefill = time.time() - t
     nxt = O.argmax_lowest(lg)
+    log(f"cpu baseline: prompt pass {t_prefill:.1f}s")
     t = time.time()
-    for _ in range(steps):
-        lg = om.decode(nxt, cache)
-        nxt = O.argmax_lowest(lg)
-    t_steps = (time.time() - t) / steps
-    # the head part of one step, timed alone (it does not scale with layers)
-    h = np.zeros((len(rows), a.d_model))
+    for j in range(1, wl.gen_len):
+        nxt = O.argmax_lowest(om.decode(nxt, cache))
+        if j % 32 == 0:
+            log(f"cpu baseline: decode step {j} at {time.time() - t:.1f}s")
+    t_decode = time.time() - t
+    # one decode step of the full batch at position prompt_len (synthetic cache contents)
+    full = O.KVCache(a.n_layers, B, a.n_heads, wl.max_seq, a.head_dim)
+    full.length = wl.prompt_len
     t = time.time()
-    for _ in range(steps):
-        om.lm_logits(h)
-    t_head = (time.time() - t) / steps
-    scale = a.n_layers / layers
-    t_row_set = (t_fold * scale + (t_prefill - t_head) * scale + t_head
-                 + (wl.gen_len - 1) * ((t_steps - t_head) * scale + t_head))
-    value = len(rows) * wl.gen_len / t_row_set
+    om.decode(prompts[:, -1], full)
+    t_full_step = time.time() - t
+    del full, cache
+    om._layers.clear()
+    blas, cores = "unknown", None
     try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    import numpy
-    blas = "unknown"
-    try:
-        cfg = numpy.show_config(mode="dicts")
-        blas = cfg.get("Build Dependencies", {}).get("blas", {}).get("name", "unknown")
+        from threadpoolctl import threadpool_info
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            blas, cores = pools[0].get("internal_api", "unknown"), pools[0].get("num_threads")
     except Exception:
         pass
+    if cores is None:
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            cores = os.cpu_count()
+    R, G = len(rows), wl.gen_len
     return {
-        "value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-        "sample": (f"rows {list(rows)} of the batch, decoder layers 0..{layers - 1} of {a.n_layers} plus head: "
-                   f"LoRA fold {t_fold:.2f}s, prompt pass {t_prefill:.2f}s, {steps} decode steps "
-                   f"{t_steps:.2f}s each (head {t_head:.3f}s); extrapolated by layer count to "
-                   f"{a.n_layers} layers and by step count to {wl.gen_len - 1} steps "
-                   f"= {t_row_set:.1f}s for {len(rows)} rows x {wl.gen_len} tokens"),
-        "blas": blas, "torch_threads": threads, "precision": "float64 with bf16 storage rounding",
+        "value": R * G / (t_prefill + t_decode), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"rows {rows} of the batch of {B}, all {a.n_layers} layers: LoRA fold of every layer "
+                   f"{t_fold:.1f}s, prompt pass ({wl.prompt_len} tokens) {t_prefill:.1f}s, {G - 1} cached "
+                   f"decode steps {t_decode:.1f}s; value = {R} x {G} generated tokens / (prompt pass + decode); "
+                   f"one decode step of the full batch of {B} at position {wl.prompt_len} {t_full_step:.2f}s"),
+        "step_tokens_per_s": R * G / (t_fold + t_prefill + t_decode),
+        "full_batch_decode_step_s": t_full_step,
+        "full_batch_decode_tokens_per_s": B / t_full_step,
+        "blas": blas, "precision": "float64 with bf16 storage rounding",
     }
 
 

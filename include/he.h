@@ -287,9 +287,12 @@ he_status he_sample(he_ctx* ctx, const float* d_logits, int32_t B, int32_t posit
 
 /* Reward scoring (page 1, pipeline section: the reward model gives each response
  * a scalar score): full causal pass over d_ids [B, S] of a HE_HEAD_SCALAR model,
- * d_reward [B] float32 = (h[S-1] proj_out^T) . score_w.  Uses the workspace.
+ * d_reward [B] float32 = y . score_w with y = h[S-1] proj_out^T (h[S-1] itself when
+ * the model has no proj_out).  d_y, when not NULL, receives y as [B, d_embed] float32.
+ * Both are caller-owned device memory, written by the end of the call's stream work.
+ * Uses the workspace.
  * Errors: HE_E_NOCACHE, HE_E_ARG, HE_E_RANGE, HE_E_UNSUPPORTED (LM-head model). */
-he_status he_score(he_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t S, float* d_reward);
+he_status he_score(he_ctx* ctx, const int32_t* d_ids, int32_t B, int32_t S, float* d_reward, float* d_y);
 
 /* Teacher-forced scoring of finished experience (page 1, pipeline section: the PPO
  * step needs, for every answer token, its log-probability under the actor and under

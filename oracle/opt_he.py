@@ -146,10 +146,18 @@ def lora_unfuse(Wf, A, B, scale: float, prec: Precision) -> np.ndarray:
 # building blocks
 # ----------------------------------------------------------------------------
 
-def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = LN_EPS) -> np.ndarray:
-    """(x - mean) / sqrt(var + eps) * g + b over the last axis, biased variance."""
+def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = LN_EPS,
+               wide=None) -> np.ndarray:
+    """(x - mean) / sqrt(var + eps) * g + b over the last axis, biased variance.
+
+    ``wide`` (default None: nothing) is applied to the two statistics as they are
+    formed; see OracleModel.wide."""
     mu = x.mean(axis=-1, keepdims=True)
+    if wide is not None:
+        mu = wide(mu)
     var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    if wide is not None:
+        var = wide(var)
     return (x - mu) / np.sqrt(var + eps) * g + b
 
 
@@ -200,6 +208,13 @@ class OracleModel:
     generator produces (Linear weights [out, in]; q, k, v packed as the rows of
     ``L{i}.qkv.w``).  With ``lora`` given, every adapted projection is folded
     (``lora_fuse``) before use; without it the base weights run.
+
+    ``wide`` is None for the method itself.  For measuring how sensitive the result
+    is to the last bits of the wide arithmetic (test infrastructure), it may be set
+    to a function that is applied to every value an implementation forms by a
+    float32 accumulation or add: the embedding sum, each projection's product
+    before its bias, the attention output before it is stored, the LayerNorm
+    statistics, the residual stream after each add, and the head's logits.
     """
 
     def __init__(self, shape, params: Dict, prec: Precision, lora: Optional[Dict] = None,
@@ -219,6 +234,10 @@ class OracleModel:
         self.fp8_decode = fp8_decode
         self._in_decode = False
         self._layers_q: Dict[int, Dict[str, np.ndarray]] = {}
+        self.wide = None
+
+    def _w(self, x: np.ndarray) -> np.ndarray:
+        return x if self.wide is None else self.wide(x)
 
     # -- parameters -----------------------------------------------------------
     def g(self, name: str) -> np.ndarray:
@@ -282,7 +301,7 @@ class OracleModel:
         e = self.g("E")[ids]
         if "proj_in" in self.params:
             e = self.prec.store(e) @ self.g("proj_in").T
-        return e + pos[None]
+        return self._w(e + pos[None])
 
     def _attend(self, i: int, lw, x: np.ndarray, pos0: int,
                 cache: Optional[KVCache]) -> np.ndarray:
@@ -290,7 +309,7 @@ class OracleModel:
         st = self.prec.store
         B, T, d = x.shape
         H, D = self.shape.n_heads, self.shape.head_dim
-        qkv = x @ lw["qkv.w"].T + lw["qkv.b"]
+        qkv = self._w(x @ lw["qkv.w"].T) + lw["qkv.b"]
         q = st(qkv[..., :d] * (1.0 / np.sqrt(D)))
         k = st(qkv[..., d:2 * d])
         v = st(qkv[..., 2 * d:])
@@ -310,26 +329,27 @@ class OracleModel:
         o = np.empty((B, H, T, D))
         for b in range(B):
             o[b], _ = causal_attention(q[b], k[b], v[b], kpos0)
-        o = st(o.transpose(0, 2, 1, 3).reshape(B, T, d))
-        return o @ lw["out.w"].T + lw["out.b"]
+        o = st(self._w(o.transpose(0, 2, 1, 3).reshape(B, T, d)))
+        return self._w(o @ lw["out.w"].T) + lw["out.b"]
 
     def _ffn(self, lw, x: np.ndarray) -> np.ndarray:
-        a = self.prec.store(np.maximum(x @ lw["fc1.w"].T + lw["fc1.b"], 0.0))
-        return a @ lw["fc2.w"].T + lw["fc2.b"]
+        a = self.prec.store(np.maximum(self._w(x @ lw["fc1.w"].T) + lw["fc1.b"], 0.0))
+        return self._w(a @ lw["fc2.w"].T) + lw["fc2.b"]
 
     def layer_forward(self, i: int, h: np.ndarray, pos0: int,
                       cache: Optional[KVCache] = None) -> np.ndarray:
         """One decoder layer on the residual stream h [B, T, d] (float64)."""
         lw = self.layer(i)
         st = self.prec.store
+        w = self._w
         if self.shape.norm == "pre":
-            h = h + self._attend(i, lw, st(layer_norm(h, lw["ln1.g"], lw["ln1.b"], self.eps)),
-                                 pos0, cache)
-            h = h + self._ffn(lw, st(layer_norm(h, lw["ln2.g"], lw["ln2.b"], self.eps)))
+            h = w(h + self._attend(i, lw, st(layer_norm(h, lw["ln1.g"], lw["ln1.b"], self.eps, self.wide)),
+                                   pos0, cache))
+            h = w(h + self._ffn(lw, st(layer_norm(h, lw["ln2.g"], lw["ln2.b"], self.eps, self.wide))))
         else:   # post-LN: normalise after each residual add; the normalised value is the stream
-            h = layer_norm(h + self._attend(i, lw, st(h), pos0, cache),
-                           lw["ln1.g"], lw["ln1.b"], self.eps)
-            h = layer_norm(h + self._ffn(lw, st(h)), lw["ln2.g"], lw["ln2.b"], self.eps)
+            h = layer_norm(w(h + self._attend(i, lw, st(h), pos0, cache)),
+                           lw["ln1.g"], lw["ln1.b"], self.eps, self.wide)
+            h = layer_norm(w(h + self._ffn(lw, st(h))), lw["ln2.g"], lw["ln2.b"], self.eps, self.wide)
         return h
 
     def hidden(self, ids, pos0: int = 0, cache: Optional[KVCache] = None) -> np.ndarray:
@@ -340,8 +360,8 @@ class OracleModel:
 
     def lm_logits(self, h: np.ndarray) -> np.ndarray:
         """Final LayerNorm, then the tied head: logits = z E^T."""
-        z = self.prec.store(layer_norm(h, self.g("lnf.g"), self.g("lnf.b"), self.eps))
-        return z @ self.g("E").T
+        z = self.prec.store(layer_norm(h, self.g("lnf.g"), self.g("lnf.b"), self.eps, self.wide))
+        return self._w(z @ self.g("E").T)
 
     # -- the two modes ----------------------------------------------------------
     def forward_full(self, ids) -> np.ndarray:
@@ -374,9 +394,16 @@ class OracleModel:
     # -- reward model -------------------------------------------------------------
     def score(self, ids) -> np.ndarray:
         """Scalar reward at the last position of each row: (h_last P_out^T) . w."""
-        h = self.hidden(np.asarray(ids), 0, None)[:, -1]
-        y = self.prec.store(h) @ self.g("proj_out").T
-        return y @ self.g("score")
+        return self.score_y(ids)[1]
+
+    def score_y(self, ids) -> Tuple[np.ndarray, np.ndarray]:
+        """(y, reward): y = h_last P_out^T [B, d_embed] and reward = y . w [B]."""
+        return self.scalar_head(self.hidden(np.asarray(ids), 0, None)[:, -1])
+
+    def scalar_head(self, h_last: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        """The reward head on the last position's stream [B, d]: (y, y . w)."""
+        y = self.prec.store(h_last) @ self.g("proj_out").T
+        return y, y @ self.g("score")
 
 
 def greedy_generate(model: OracleModel, prompts, gen_len: int, max_seq: int,

@@ -14,22 +14,57 @@ from transformer_decode_amd import he
 BF16_ABS_TOL = 3e-2       # bf16 workloads: max |logit difference| per row and step
 FP32_REL_TOL = 1e-3       # fp32 workload: max |difference| <= 1e-3 * max |oracle logit|
 MARGIN = 1e-2             # greedy picks are compared where the oracle's top-2 gap exceeds this
-# Where the oracle itself moves by more than BF16_ABS_TOL under a float32-sized input
-# perturbation (tests/golden/oracle_sensitivity.json), the bound is this multiple of
-# that measured floor: the GPU's float32 accumulation perturbs every layer, not
-# only the input.
-FLOOR_FACTOR = 1.5
+# Full-depth bf16 workloads: where the oracle's own sensitivity to float32-sized errors
+# in its wide arithmetic exceeds BF16_ABS_TOL, the bound is the level a further
+# float32-accurate evaluation stays under: the measured mean m of the perturbed
+# copies' largest logit differences at that row and step, plus FLOOR_SIGMAS standard
+# deviations (m times the coefficient of variation c pooled over the workload's
+# copies, rows and steps).  A largest difference over 50272 logits follows an
+# extreme-value (Gumbel) law, under which mean + 6 sd is exceeded with probability
+# about 2.6e-4 per comparison.
+FLOOR_SIGMAS = 6.0
 _GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_sensitivity.json")
 
 
-def oracle_floor(name, row, step):
-    """The oracle's measured self-sensitivity at (row, step) of a workload, or None."""
+def _floor_entry(name):
     if not os.path.exists(_GOLDEN):
         return None
-    entry = json.load(open(_GOLDEN)).get(name)
-    if not entry or row not in entry["rows"] or step not in entry["steps"]:
+    return json.load(open(_GOLDEN)).get(name)
+
+
+def floor_stats(name):
+    """(means [rows][steps], pooled coefficient of variation) of a workload's stored
+    perturbed copies, or None.  means: the larger of the 2^-24 and 2^-16 groups' means."""
+    e = _floor_entry(name)
+    if not e or "per_copy_max_abs_dlogit" not in e:
         return None
-    return entry["max_abs_dlogit"][entry["rows"].index(row)][entry["steps"].index(step)]
+    a = np.asarray(e["per_copy_max_abs_dlogit"], dtype=np.float64)        # [copies, rows, steps]
+    b = np.asarray(e["gpu_per_copy_max_abs_dlogit"], dtype=np.float64)
+    allc = np.concatenate([a, b], axis=0)
+    rel = allc / allc.mean(axis=0, keepdims=True)
+    c = float(rel.std(ddof=1))
+    return np.maximum(a.mean(axis=0), b.mean(axis=0)), c, e["rows"], e["steps"]
+
+
+def oracle_floor(name, row, step):
+    """The logit bound the oracle's own sensitivity sets at (row, step), or None."""
+    st_ = floor_stats(name)
+    if st_ is None:
+        return None
+    means, c, rows, steps = st_
+    if row not in rows or step not in steps:
+        return None
+    return float(means[rows.index(row), steps.index(step)] * (1.0 + FLOOR_SIGMAS * c))
+
+
+def oracle_floor_pooled(name, step):
+    """The largest oracle_floor over the workload's stored rows at `step` (for rows
+    that were not sampled: the level is a property of the model, not of the row), or
+    None."""
+    st_ = floor_stats(name)
+    if st_ is None or step not in st_[3]:
+        return None
+    return max(oracle_floor(name, r, step) for r in st_[2])
 
 
 def log(msg):
@@ -53,7 +88,11 @@ def top2_margin(logits):
 
 
 def check_logits(gpu, ref, shape, what="", floors=None):
-    """floors: per-row oracle self-sensitivity (or None) for the bf16 bound."""
+    """Max |logit difference| per row against the workload's bound, and greedy picks.
+    floors: per row, the oracle-sensitivity bound (oracle_floor) or None; the bf16
+    bound is the larger of BF16_ABS_TOL and it.  Picks are compared where the oracle's
+    top-2 gap exceeds MARGIN and twice the row's measured largest difference: a pick
+    can only change where the gap is at most twice the largest change of a logit."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     err = np.abs(gpu - ref).max(axis=-1)
@@ -62,12 +101,12 @@ def check_logits(gpu, ref, shape, what="", floors=None):
     else:
         bound = np.full(err.shape, BF16_ABS_TOL)
         if floors is not None:
-            bound = np.maximum(bound, FLOOR_FACTOR * np.array([f if f is not None else 0.0 for f in floors]))
+            bound = np.maximum(bound, np.array([f if f is not None else 0.0 for f in floors]))
     bad = err > bound
-    log(f"{what}: max |dlogit| {err.max():.3e} (bound {bound.min():.3e})")
-    assert not bad.any(), f"{what}: max |dlogit| {err.max():.3e} over bound {bound.max():.3e} at rows {np.nonzero(bad)}"
-    # greedy picks agree wherever the oracle's choice is clear
-    clear = top2_margin(ref) > MARGIN
+    log(f"{what}: max |dlogit| {err.max():.3e} per row {np.array2string(err, precision=4)} "
+        f"(bounds {np.array2string(bound, precision=4)})")
+    assert not bad.any(), f"{what}: max |dlogit| {err.max():.3e} over bound at rows {np.nonzero(bad)}"
+    clear = top2_margin(ref) > np.maximum(MARGIN, 2 * err)
     assert (gpu.argmax(-1)[clear] == ref.argmax(-1)[clear]).all(), f"{what}: argmax mismatch"
     return float(err.max())
 
@@ -126,14 +165,14 @@ class GpuRun:
         self.eng.close()
 
 
-def greedy_prefix_agrees(gpu_picks, oracle_picks, oracle_logits):
+def greedy_prefix_agrees(gpu_picks, oracle_picks, oracle_logits, margin=MARGIN):
     """Free-running picks must agree up to the first step where the oracle's own
-    choice is not clear (top-2 gap <= MARGIN); returns the number compared."""
+    choice is not clear (top-2 gap <= margin); returns the number compared."""
     compared = 0
     B, G = oracle_picks.shape
     for b in range(B):
         for j in range(G):
-            if top2_margin(oracle_logits[j][b]) <= MARGIN:
+            if top2_margin(oracle_logits[j][b]) <= margin:
                 break
             assert gpu_picks[b, j] == oracle_picks[b, j], f"row {b} step {j}: {gpu_picks[b, j]} vs {oracle_picks[b, j]}"
             compared += 1

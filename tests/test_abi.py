@@ -240,7 +240,7 @@ def test_reward_model_only_scores():
     e = _engine(wl.reward)
     ctx, P = e.ctx, 0x1234
     he.he_retake_cache(ctx, 128, 512)
-    he.he_score(ctx, P, 128, 512, P)
+    he.he_score(ctx, P, 128, 512, P, P)
     assert _status(he.he_prefill, ctx, P, 2, 16, P) == he.HE_E_UNSUPPORTED
     assert _status(he.he_logprobs, ctx, P, 2, 16, 8, P) == he.HE_E_UNSUPPORTED
     assert _status(he.he_sample, ctx, P, 2, 0, None, P, 0) == he.HE_E_UNSUPPORTED

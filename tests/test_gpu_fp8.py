@@ -190,3 +190,41 @@ def test_opt125m_fp8_top_p_generation_follows_the_rule_each_step():
     run.close()
     assert np.array_equal(a_t, np.stack(bt, axis=1))
     assert np.array_equal(a_l.view(np.uint32), np.stack(bl, axis=1).view(np.uint32))
+
+
+def test_opt125m_fp8_toggle_recaptures_graph():
+    """FP8 on -> generate -> off -> on -> generate: switching FP8 decode off frees the E4M3
+    copy and switching it on makes a new one at new addresses, so a decode graph captured
+    before must not be replayed.  Between off and on the freed memory is taken by a
+    buffer of NaN codes (0xFF), so a replayed stale graph would read them.  Graph replay
+    must equal direct launches bit for bit, both generations."""
+    wl = synth.WORKLOADS["opt125m"]
+    params = synth.model_params(wl.actor)
+    lora = synth.lora_params(wl.actor, wl.lora_rank)
+    prompts = synth.prompts(wl)
+    d, F_ = wl.actor.d_model, wl.actor.d_ffn
+    f8_bytes = wl.actor.n_layers * (4 * d * d + 2 * d * F_ + 4 * (6 * d + F_))
+    outs = {}
+    for name, use_graph in (("graph", True), ("direct", False)):
+        run = GpuRun(wl, params, use_graph=use_graph)
+        lt = run.lora(lora)
+        with torch.cuda.stream(run.stream):
+            he.he_fuse_lora(run.ctx, lt)
+            he.he_retake_cache(run.ctx, wl.batch, wl.max_seq)
+            he.he_set_fp8_decode(run.ctx, True)
+        first = run.generate(prompts, 16)
+        with torch.cuda.stream(run.stream):
+            he.he_set_fp8_decode(run.ctx, False)
+            he.he_sync(run.ctx)
+        junk = torch.full((f8_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(run.stream):
+            he.he_set_fp8_decode(run.ctx, True)
+        second = run.generate(prompts, 16)
+        del junk
+        outs[name] = (first, second)
+        run.close()
+    log("fp8 toggle: graph and direct generations compared")
+    assert np.array_equal(outs["graph"][0], outs["direct"][0])
+    assert np.array_equal(outs["graph"][1], outs["direct"][1])
+    assert np.array_equal(outs["graph"][0], outs["graph"][1])

@@ -309,3 +309,108 @@ def test_sample_batch_one(head_only):
     want_t, want_lp, ok = _robust(x.numpy().astype(np.float64), 0.9, 5, np.arange(1), 40, 0.8)
     run.close()
     assert ok[0] and tok.item() == want_t[0] and abs(lp.item() - want_lp[0]) <= LP_TOL * max(1.0, abs(want_lp[0]))
+
+
+# ------------------------------------------------------------------------------------
+# greedy ties: the lowest index wins (the rule's reading of argmax)
+# ------------------------------------------------------------------------------------
+
+def _tie_logits(V):
+    """[8, V] float32 logits with exact ties at the maximum: inside one 128-column
+    block, across adjacent blocks, across the two halves of a block, at the last
+    column, over the whole row, and a three-way tie."""
+    g = np.random.default_rng(77)
+    x = (-g.random((8, V))).astype(np.float32)           # values in (-1, 0]
+    ties = {0: [5, 100], 1: [127, 128], 2: [1000, V - 1], 3: [V - 1], 5: [V - 2, V - 1], 6: [63, 64],
+            7: [200, 7000, V - 100]}
+    for r, cols in ties.items():
+        x[r, cols] = 3.0
+    x[4, :] = 1.0
+    return x
+
+
+@pytest.mark.parametrize("pos", [0, 511])
+def test_sample_greedy_ties_pick_lowest_index(head_only, pos):
+    """he_sample at temperature 0 on logits with exact ties at the maximum: the pick
+    is the lowest tied index (oracle argmax_lowest), its log-probability that of
+    log softmax at that index."""
+    wl, params = head_only
+    V = wl.actor.vocab
+    x = _tie_logits(V)
+    B = x.shape[0]
+    want = O.argmax_lowest(x.astype(np.float64))
+    assert list(want) == [5, 127, 1000, V - 1, 0, V - 2, 63, 200]
+    xs = x.astype(np.float64)
+    want_lp = xs[np.arange(B), want] - (xs.max(1) + np.log(np.exp(xs - xs.max(1, keepdims=True)).sum(1)))
+    run = GpuRun(wl, params)
+    d_x = torch.from_numpy(x).cuda()
+    tok = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    lp = torch.full((B,), float("nan"), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(run.stream):
+        he.he_retake_cache(run.ctx, B, 16)
+        he.he_sample(run.ctx, d_x.data_ptr(), B, pos, None, tok.data_ptr(), lp.data_ptr())
+        he.he_sync(run.ctx)
+    got, got_lp = tok.cpu().numpy(), lp.cpu().numpy()
+    run.close()
+    log(f"greedy ties at position {pos}: picks {got}")
+    assert np.array_equal(got, want), (got, want)
+    assert np.allclose(got_lp, want_lp, atol=LP_TOL), (got_lp, want_lp)
+
+
+def test_opt125m_lm_head_tie_from_duplicated_embedding_rows():
+    """A tie made inside the tied LM head: row b of the embedding is set equal to row a,
+    where a is the oracle's clear greedy pick after the prompt of batch row r and b < a
+    appears in no prompt of the batch.  Then logit b equals logit a exactly and the
+    prompt pass must pick b.  For one sampled row b lies in a's 64-row block of the head
+    (the head's per-workgroup pick), for another in an earlier block (the fixed-order
+    merge of block picks)."""
+    wl = synth.WORKLOADS["opt125m"]
+    params = synth.model_params(wl.actor)
+    lora = synth.lora_params(wl.actor, wl.lora_rank)
+    prompts = synth.prompts(wl)
+    B, S, V = wl.batch, wl.prompt_len, wl.actor.vocab
+    om = O.OracleModel(wl.actor, params, precision(wl.actor), lora=lora, lora_scale=wl.lora_scale)
+    lg, _ = om.prefill(prompts.numpy(), wl.max_seq)
+    s = np.sort(lg, axis=1)
+    clear = [r for r in range(B) if s[r, -1] - s[r, -2] > 0.05]
+    assert len(clear) >= 2
+    used = set(prompts.numpy().ravel().tolist())
+    picks = {}                                            # batch row -> (a, b)
+
+    def take(r, same_block):
+        a = int(lg[r].argmax())
+        lo = (a // 64) * 64
+        cands = range(a - 1, lo - 1, -1) if same_block else range(lo - 1, -1, -1)
+        taken = {v for ab in picks.values() for v in ab} | {int(lg[q].argmax()) for q in clear}
+        b = next((c for c in cands if c not in used and c not in taken), None)
+        if b is not None:
+            picks[r] = (a, b)
+        return b is not None
+
+    assert any(take(r, True) for r in clear), "no free index below a pick inside its block"
+    assert any(take(r, False) for r in clear if r not in picks), "no free index in an earlier block"
+    E = params["E"].clone()
+    for r, (a, b) in picks.items():
+        E[b] = E[a]
+    tied = dict(params)
+    tied["E"] = E
+    run = GpuRun(wl, tied)
+    lt = run.lora(lora)
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    lgt = torch.empty(B, V, dtype=torch.float32, device="cuda")
+    ids = prompts.cuda()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(run.stream):
+        he.he_fuse_lora(run.ctx, lt)
+        he.he_retake_cache(run.ctx, B, wl.max_seq)
+        he.he_prefill(run.ctx, ids.data_ptr(), B, S, nxt.data_ptr(), lgt.data_ptr())
+        he.he_sync(run.ctx)
+    got, glg = nxt.cpu().numpy(), lgt.cpu().numpy()
+    run.close()
+    for r, (a, b) in picks.items():
+        log(f"LM-head tie, row {r}: rows {b} and {a} of E equal; GPU logits {glg[r, b]!r} / {glg[r, a]!r}, "
+            f"pick {got[r]}")
+        assert glg[r, b] == glg[r, a], "duplicated head rows gave different logits"
+        assert glg[r].max() == glg[r, a], "the duplicated row is not the maximum"
+        assert got[r] == b, (r, got[r], a, b)

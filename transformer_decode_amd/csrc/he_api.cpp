@@ -56,6 +56,7 @@ struct he_ctx {
   std::vector<he_layer_weights> layers;
   hipStream_t stream = nullptr;
   bool own_stream = false;
+  int device = 0;                 // the GPU current at he_create
   int dt = DT_BF16, L = 0, d = 0, H = 0, D = 0, F = 0, V = 0, de = 0;
   float q_scale = 1.f;
   bool validate_only = false, use_graph = true;
@@ -470,7 +471,7 @@ static void enqueue_step(he_ctx* c, int B, bool want_logits, int pos) {
 }
 
 // Full causal pass of a scalar-head model, reward at the last position.
-static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* reward) {
+static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* reward, float* y) {
   const int M = B * S, d = c->d, F = c->F, dt = c->dt, de = c->de;
   const float eps = c->desc.ln_eps;
   const size_t es = esize(dt);
@@ -543,7 +544,7 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
     xs = 1;
   }
   run_k(c, HE_K_SCORE, (double)de * d * es, 2.0 * B * de * d,
-        [&] { launch_score(dt, c->x, c->wt.proj_out, c->wt.score_w, reward, B, xs, d, de, st); });
+        [&] { launch_score(dt, c->x, c->wt.proj_out, c->wt.score_w, reward, y, B, xs, d, de, st); });
 }
 
 // ------------------------------------------------------------------------------------
@@ -618,6 +619,10 @@ he_status he_create(const he_model_desc* desc, const he_weight_table* w, void* h
   const char* ng = std::getenv("HE_NO_GRAPH");
   c->use_graph = D.use_graph && !(ng && ng[0] == '1');
   if (!c->validate_only) {
+    if (hipGetDevice(&c->device) != hipSuccess) {
+      delete c;
+      return HE_E_HIP;
+    }
     if (hip_stream) {
       c->stream = (hipStream_t)hip_stream;
     } else {
@@ -691,6 +696,8 @@ he_status he_set_fp8_decode(he_ctx* c, int32_t enable) {
   if (c->failed) return set_err(c, HE_E_HIP, "context failed earlier: %s", c->err.c_str());
   if (!enable) {
     c->prefilled = false;   // decode plans depend on the weight format: a new prompt pass
+    // captured decode graphs hold the copy's addresses as kernel arguments
+    drop_graphs(c);
     if (c->f8buf && !c->validate_only) {
       HIP_TRY(c, hipStreamSynchronize(c->stream));
       hipFree(c->f8buf);
@@ -720,6 +727,7 @@ he_status he_set_fp8_decode(he_ctx* c, int32_t enable) {
     c->f8_on = true;
     return HE_OK;
   }
+  drop_graphs(c);   // a new copy at new addresses: no captured graph may point at an old one
   char* buf = nullptr;
   hipError_t e = hipMalloc((void**)&buf, std::max<size_t>(off, 256));
   if (e != hipSuccess) {
@@ -1124,42 +1132,69 @@ he_status he_generate_ex(he_ctx* c, const int32_t* d_prompt, int32_t B, int32_t 
   return keep.done(generate(c, d_prompt, B, S, S_g, d_out, d_logprobs));
 }
 
+// The pick rule of smp on caller logits [B][V]: per-block partials in (best_val,
+// best_idx, and for log-probabilities best_lg / blk_max / blk_sum), the position pair
+// in spos.  Checks come first; nothing is enqueued on a refused call.
+struct PickScratch {
+  int32_t* spos;
+  float* best_val;
+  int32_t* best_idx;
+  float* best_lg;
+  float* blk_max;
+  float* blk_sum;
+};
+
+static he_status sample_checks(he_ctx* c, const float* d_logits, int32_t B, int32_t position,
+                               const he_sampling* smp, int32_t* d_tokens, float* d_logprobs, int max_b,
+                               float* it, uint64_t* seed, float* tp, bool* want_lp) {
+  if (c->failed) return set_err(c, HE_E_HIP, "context failed earlier: %s", c->err.c_str());
+  if (c->desc.head != HE_HEAD_LM) return set_err(c, HE_E_UNSUPPORTED, "sampling needs an LM-head model");
+  if (!d_logits || !d_tokens) return set_err(c, HE_E_ARG, "NULL buffer");
+  if (B < 1 || B > max_b) return set_err(c, HE_E_ARG, "batch %d outside 1..%d", B, max_b);
+  if (position < 0) return set_err(c, HE_E_ARG, "position %d < 0", position);
+  // the rule of this call only: the context's own (used by he_decode_step) is kept
+  RuleKeep keep(c);
+  he_status s = set_rule(c, smp, d_logprobs != nullptr);
+  *it = c->inv_temp; *tp = c->top_p; *seed = c->seed; *want_lp = c->want_logp;
+  keep.restore();
+  return s;
+}
+
+static he_status enqueue_sample(he_ctx* c, const float* d_logits, int32_t B, int32_t position, float it,
+                                uint64_t seed, float tp, bool want_lp, const PickScratch& ps,
+                                int32_t* d_tokens, float* d_logprobs) {
+  hipStream_t st = c->stream;
+  SampleArgs smpa;
+  smpa.inv_temp = it;
+  smpa.seed = seed;
+  if (want_lp) { smpa.best_lg = ps.best_lg; smpa.blk_max = ps.blk_max; smpa.blk_sum = ps.blk_sum; }
+  launch_set_i32(ps.spos, position - 1, st);
+  if (tp < 1.f) {
+    launch_set_i32(ps.spos + 1, position, st);
+    launch_topp_finalize(d_logits, B, c->V, smpa, tp, nullptr, d_tokens, d_logprobs, 0, ps.spos + 1,
+                         nullptr, st);
+  } else {
+    const int nb = (c->V + 127) / 128;
+    launch_reduce_argmax(d_logits, 1, B, c->V, nullptr, ps.best_val, ps.best_idx, nb, ps.spos, ps.spos + 1,
+                         smpa, st);
+    launch_argmax_finalize(ps.best_val, ps.best_idx, smpa, nb, B, nullptr, d_tokens,
+                           want_lp ? d_logprobs : nullptr, 0, ps.spos + 1, nullptr, nullptr, st);
+  }
+  return check_launch(c, "sample launch");
+}
+
 he_status he_sample(he_ctx* c, const float* d_logits, int32_t B, int32_t position, const he_sampling* smp,
                     int32_t* d_tokens, float* d_logprobs) {
   if (!c) return HE_E_ARG;
   he_status s = check_compute(c);
   if (s != HE_OK) return s;
-  if (c->desc.head != HE_HEAD_LM) return set_err(c, HE_E_UNSUPPORTED, "sampling needs an LM-head model");
-  if (!d_logits || !d_tokens) return set_err(c, HE_E_ARG, "NULL buffer");
-  if (B < 1 || B > c->max_batch) return set_err(c, HE_E_ARG, "batch %d outside 1..%d", B, c->max_batch);
-  if (position < 0) return set_err(c, HE_E_ARG, "position %d < 0", position);
-  // the rule of this call only: the context's own (used by he_decode_step) is kept
-  RuleKeep keep(c);
-  s = set_rule(c, smp, d_logprobs != nullptr);
-  const float it = c->inv_temp, tp = c->top_p;
-  const uint64_t seed = c->seed;
-  const bool want_lp = c->want_logp;
-  keep.restore();
-  if (s != HE_OK) return s;
-  if (c->validate_only) return HE_OK;
-  hipStream_t st = c->stream;
-  SampleArgs smpa;
-  smpa.inv_temp = it;
-  smpa.seed = seed;
-  if (want_lp) { smpa.best_lg = c->best_lg; smpa.blk_max = c->blk_max; smpa.blk_sum = c->blk_sum; }
-  launch_set_i32(c->spos, position - 1, st);
-  if (tp < 1.f) {
-    launch_set_i32(c->spos + 1, position, st);
-    launch_topp_finalize(d_logits, B, c->V, smpa, tp, nullptr, d_tokens, d_logprobs, 0, c->spos + 1,
-                         nullptr, st);
-  } else {
-    const int nb = (c->V + 127) / 128;
-    launch_reduce_argmax(d_logits, 1, B, c->V, nullptr, c->best_val, c->best_idx, nb, c->spos, c->spos + 1,
-                         smpa, st);
-    launch_argmax_finalize(c->best_val, c->best_idx, smpa, nb, B, nullptr, d_tokens,
-                           want_lp ? d_logprobs : nullptr, 0, c->spos + 1, nullptr, nullptr, st);
-  }
-  return check_launch(c, "sample launch");
+  float it = 0.f, tp = 1.f;
+  uint64_t seed = 0;
+  bool want_lp = false;
+  s = sample_checks(c, d_logits, B, position, smp, d_tokens, d_logprobs, c->max_batch, &it, &seed, &tp, &want_lp);
+  if (s != HE_OK || c->validate_only) return s;
+  const PickScratch ps{c->spos, c->best_val, c->best_idx, c->best_lg, c->blk_max, c->blk_sum};
+  return enqueue_sample(c, d_logits, B, position, it, seed, tp, want_lp, ps, d_tokens, d_logprobs);
 }
 
 // Teacher-forced scoring: prompt pass over the whole sequence, final LayerNorm of the
@@ -1215,7 +1250,7 @@ he_status he_logprobs(he_ctx* c, const int32_t* d_seq, int32_t B, int32_t S, int
   return check_launch(c, "logprobs launch");
 }
 
-he_status he_score(he_ctx* c, const int32_t* d_ids, int32_t B, int32_t S, float* d_reward) {
+he_status he_score(he_ctx* c, const int32_t* d_ids, int32_t B, int32_t S, float* d_reward, float* d_y) {
   if (!c) return HE_E_ARG;
   he_status s = check_compute(c);
   if (s != HE_OK) return s;
@@ -1225,7 +1260,7 @@ he_status he_score(he_ctx* c, const int32_t* d_ids, int32_t B, int32_t S, float*
   if (S < 1) return set_err(c, HE_E_ARG, "length %d < 1", S);
   if (S > c->max_seq) return set_err(c, HE_E_RANGE, "length %d > max_seq %d", S, c->max_seq);
   if (c->validate_only) return HE_OK;
-  enqueue_score(c, d_ids, B, S, d_reward);
+  enqueue_score(c, d_ids, B, S, d_reward, d_y);
   c->prefilled = false;   // the cache now holds the scored sequences
   return check_launch(c, "score launch");
 }

@@ -763,8 +763,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x,
                                                     const T* __restrict__ Pout,
                                                     const T* __restrict__ w,
-                                                    float* __restrict__ reward, int S, int d,
-                                                    int de) {
+                                                    float* __restrict__ reward, float* __restrict__ y,
+                                                    int S, int d, int de) {
   extern __shared__ float sm[];
   float* xs = sm;          // [d]
   float* ys = sm + d;      // [de]
@@ -785,21 +785,23 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x,
     for (int j = tid; j < de; j += 256) ys[j] = xs[j];
   }
   __syncthreads();
+  if (y)
+    for (int j = tid; j < de; j += 256) y[(size_t)b * de + j] = ys[j];
   float part = 0.f;
   for (int j = tid; j < de; j += 256) part = fmaf(ys[j], ld(w + j), part);
   float tot = block_sum(part, red);
   if (tid == 0) reward[b] = tot;
 }
 
-void launch_score(int dt, const void* x, const void* proj_out, const void* w, float* reward, int B,
-                  int S, int d, int de, hipStream_t st) {
+void launch_score(int dt, const void* x, const void* proj_out, const void* w, float* reward, float* y,
+                  int B, int S, int d, int de, hipStream_t st) {
   size_t lds = (size_t)(d + de) * sizeof(float);
   if (dt == DT_BF16)
     score_kernel<bf16><<<B, 256, lds, st>>>((const bf16*)x, (const bf16*)proj_out, (const bf16*)w,
-                                            reward, S, d, de);
+                                            reward, y, S, d, de);
   else
     score_kernel<float><<<B, 256, lds, st>>>((const float*)x, (const float*)proj_out, (const float*)w,
-                                             reward, S, d, de);
+                                             reward, y, S, d, de);
 }
 
 __global__ void set_i32_kernel(int32_t* p, int32_t v) { *p = v; }

@@ -235,8 +235,9 @@ void launch_attn_decode_q(int dt, const void* q, const void* k_cache, const void
 void launch_set_i32(int32_t* p, int32_t v, hipStream_t st);
 
 // ---- reward head -------------------------------------------------------------------------
-// reward[b] = sum_j (sum_k x[b*S + S-1][k] Pout[j][k]) * w[j]
-void launch_score(int dt, const void* x, const void* proj_out, const void* w, float* reward,
+// y[b][j] = sum_k x[b*S + S-1][k] Pout[j][k] (the state itself without Pout);
+// reward[b] = sum_j y[b][j] w[j]; y (nullable) receives [B][de] float32.
+void launch_score(int dt, const void* x, const void* proj_out, const void* w, float* reward, float* y,
                   int B, int S, int d, int de, hipStream_t st);
 
 }  // namespace he

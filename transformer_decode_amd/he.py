@@ -78,7 +78,7 @@ _SIGS = {
     "he_decode_step": (_i32, [_vp, _vp, _vp, _vp]),
     "he_generate": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
     "he_generate_ex": (_i32, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
-    "he_score": (_i32, [_vp, _vp, _i32, _i32, _vp]),
+    "he_score": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "he_sample": (_i32, [_vp, _vp, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
     "he_set_fp8_decode": (_i32, [_vp, _i32]),
     "he_fp8_export": (_i32, [_vp, _i32, _i32, _vp, _vp]),
@@ -182,8 +182,8 @@ def he_fp8_export(ctx, layer: int, proj: int, d_codes: int, d_scales: int):
     return _check(lib().he_fp8_export(ctx, layer, proj, _vp(d_codes), _vp(d_scales)), ctx)
 
 
-def he_score(ctx, d_ids: int, B: int, S: int, d_reward: int):
-    return _check(lib().he_score(ctx, _vp(d_ids), B, S, _vp(d_reward)), ctx)
+def he_score(ctx, d_ids: int, B: int, S: int, d_reward: int, d_y: int = 0):
+    return _check(lib().he_score(ctx, _vp(d_ids), B, S, _vp(d_reward), _vp(d_y)), ctx)
 
 
 def he_logprobs(ctx, d_seq: int, B: int, S: int, S_p: int, d_logprobs: int):
