@@ -188,13 +188,13 @@ def counters_summary(fetch_csv, write_csv, workload, command):
     return out
 
 
-MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16",)
 
 
 def mfma_summary(csv_path, workload, command):
     """Per-kernel MFMA work from one rocprofv3 --pmc pass of MFMA_COUNTERS: bf16 MFMA
-    flops = MOPS x 512 (to set beside the algorithmic 2 M N K), and the raw ratio of
-    MFMA busy cycles to GPU active cycles as the counters report them."""
+    flops = MOPS x 512 per dispatch, to set beside the algorithmic 2 M N K.  The rate
+    against peak comes from kernel time, not from a busy-cycle ratio."""
     import csv
     disp = {}
     for r in csv.DictReader(open(csv_path)):
@@ -202,22 +202,19 @@ def mfma_summary(csv_path, workload, command):
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     per = {}
     for d in disp.values():
-        if not all(c in d for c in MFMA_COUNTERS) or d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] <= 0:
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" not in d or d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] <= 0:
             continue
-        e = per.setdefault(d["name"], [0, 0.0, 0.0, 0.0])
+        e = per.setdefault(d["name"], [0, 0.0])
         e[0] += 1
         e[1] += d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
-        e[2] += d["SQ_VALU_MFMA_BUSY_CYCLES"]
-        e[3] += d["GRBM_GUI_ACTIVE"] * 256 * 4
-    lines = [f"# MFMA work and utilisation, {workload}", "", "Command (run from the repository root, output under "
+    lines = [f"# MFMA work, {workload}", "", "Command (run from the repository root, output under "
              "gpurun_out/):", "", "```", command, "```", "",
-             "bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per dispatch. busy / active = "
-             "SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE summed over the kernel's dispatches, as the counters "
-             "report them (their normalisation over XCDs, CUs and SIMDs is not restated here; the rate against "
-             "peak comes from kernel time).", "",
-             "| kernel | dispatches | MFMA TFLOP per dispatch | MFMA busy / GPU active |", "|---|---|---|---|"]
-    for name, (n, fl, busy, act) in sorted(per.items(), key=lambda kv: -kv[1][1]):
-        lines.append(f"| `{name[:100]}` | {n} | {fl / n / 1e12:.3f} | {busy / (act / 1024):.1f} |")
+             "bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per dispatch (the counter counts 512-flop "
+             "units): the work the MFMAs did, to compare with the algorithmic 2 M N K of each GEMM. The rate "
+             "against the bf16 peak is taken from kernel time (kernel summaries and the bench line).", "",
+             "| kernel | dispatches | MFMA TFLOP per dispatch |", "|---|---|---|"]
+    for name, (n, fl) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| `{name[:100]}` | {n} | {fl / n / 1e12:.4f} |")
     return "\n".join(lines) + "\n"
 
 
@@ -243,6 +240,81 @@ def stats_summary(stats_csv, workload, command):
     return "\n".join(lines) + "\n"
 
 
+def two_round_sequence(wl, a, dev, ldev, prompts, seed):
+    """The largest workload's sequence (page 2, section 3: release the workspace after
+    generation, retake it before the next): round 1 fuse, generate, unfuse, release;
+    round 2 retake, fuse, generate, unfuse, release; then the reward model scores the
+    round-2 experience (prompt + answer).  Times of each call, the memory the release
+    returns, and whether round 2 repeats round 1's tokens (same adapters)."""
+    import torch
+
+    import synth
+    from transformer_decode_amd import he
+
+    B, S, G = wl.batch, wl.prompt_len, wl.gen_len
+    eng = he.Engine(a, dev)
+    ctx, st = eng.ctx, eng.stream
+    lt, _keep = eng.lora(ldev, wl.lora_rank, wl.lora_alpha)
+    out = [torch.empty(B, G, dtype=torch.int32, device="cuda") for _ in range(2)]
+    rec = {}
+    torch.cuda.synchronize()
+    t_all = time.time()
+    for rnd in (1, 2):
+        free0 = torch.cuda.mem_get_info()[0]
+        t = time.time()
+        with torch.cuda.stream(st):
+            he.he_retake_cache(ctx, B, wl.max_seq)
+            he.he_sync(ctx)
+        rec[f"round{rnd}_retake_ms"] = (time.time() - t) * 1e3
+        E = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        with torch.cuda.stream(st):
+            E[0].record(st)
+            he.he_fuse_lora(ctx, lt)
+            E[1].record(st)
+            he.he_generate(ctx, prompts.data_ptr(), B, S, G, out[rnd - 1].data_ptr())
+            E[2].record(st)
+            he.he_unfuse_lora(ctx, lt)
+            E[3].record(st)
+            he.he_sync(ctx)
+        free1 = torch.cuda.mem_get_info()[0]
+        t = time.time()
+        with torch.cuda.stream(st):
+            he.he_release_cache(ctx)
+            he.he_sync(ctx)
+        rec[f"round{rnd}_release_ms"] = (time.time() - t) * 1e3
+        free2 = torch.cuda.mem_get_info()[0]
+        rec[f"round{rnd}_fuse_ms"] = E[0].elapsed_time(E[1])
+        rec[f"round{rnd}_generate_ms"] = E[1].elapsed_time(E[2])
+        rec[f"round{rnd}_unfuse_ms"] = E[2].elapsed_time(E[3])
+        rec[f"round{rnd}_gen_tokens_per_s"] = B * G / (E[1].elapsed_time(E[2]) / 1e3)
+        rec[f"round{rnd}_workspace_GB"] = (free0 - free1) / 1e9
+        rec[f"round{rnd}_returned_GB"] = (free2 - free1) / 1e9
+    rec["round2_equals_round1"] = bool(torch.equal(out[0], out[1]))
+    eng.close()
+    rs = wl.reward
+    rdev = {k: v.cuda() for k, v in synth.model_params(rs, seed, prefix="rm.").items()}
+    exp = torch.cat([prompts, out[1]], dim=1).to(torch.int32).contiguous()
+    reward = torch.empty(B, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    eng3 = he.Engine(rs, rdev)
+    E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(eng3.stream):
+        he.he_retake_cache(eng3.ctx, B, S + G)
+        E[0].record(eng3.stream)
+        he.he_score(eng3.ctx, exp.data_ptr(), B, S + G, reward.data_ptr())
+        E[1].record(eng3.stream)
+        he.he_release_cache(eng3.ctx)
+        he.he_sync(eng3.ctx)
+    eng3.close()
+    torch.cuda.synchronize()
+    rec["reward_scoring_ms"] = E[0].elapsed_time(E[1])
+    rec["rewards_finite"] = bool(torch.isfinite(reward).all().item())
+    rec["wall_s"] = time.time() - t_all
+    del rdev
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +324,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-phase / per-kernel passes")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="keep the per-phase and per-kernel passes, skip the other modes (sampling, FP8 decode, "
+                         "scoring, the no-graph decode, the reward model)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--trace-steps", type=int, default=0,
                     help="for counter collection: a calibration copy, then fuse + prefill + N decode "
@@ -475,122 +550,127 @@ def main():
                            "launches": s.launches}
         log(f"roofline: {json.dumps(res['roofline'])}")
 
-        # sampled generation (temperature 0.7, Gumbel-max with Philox4x64-10) with per-token
-        # log-probabilities, same shape and fused weights: whole-generation time beside the
-        # greedy one, and the LM head's time per launch in each mode
-        with torch.cuda.stream(st):
-            lpb = torch.empty(B, G, dtype=torch.float32, device="cuda")
-            smp = he.he_sampling(0.7, 1234)
-            E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            he.he_fuse_lora(ctx, lt)
-            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp, out.data_ptr(), lpb.data_ptr())  # graph capture
-            E[0].record(st)
-            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp, out.data_ptr(), lpb.data_ptr())
-            E[1].record(st)
-            # the same with a top-p 0.9 nucleus (graph captured by the first call)
-            smp_p = he.he_sampling(0.7, 1234, 0.9)
-            Ep = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp_p, out.data_ptr(), lpb.data_ptr())
-            Ep[0].record(st)
-            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp_p, out.data_ptr(), lpb.data_ptr())
-            Ep[1].record(st)
-            he.he_kernel_timer(ctx, he.HE_K_LMHEAD, True)
-            he.he_generate_ex(ctx, prompts.data_ptr(), B, S, 8, smp, out.data_ptr(), lpb.data_ptr())
-            lm_s = he.he_kernel_stats(ctx, he.HE_K_LMHEAD)
-            he.he_kernel_timer(ctx, he.HE_K_LMHEAD, False)
-            he.he_unfuse_lora(ctx, lt)
-            he.he_sync(ctx)
-            torch.cuda.synchronize()
-        t_smp = E[0].elapsed_time(E[1]) / 1e3
-        t_topp = Ep[0].elapsed_time(Ep[1]) / 1e3
-        lps = lpb.cpu().numpy()
-        res["sampled"] = {
-            "temperature": 0.7, "gen_ms": t_smp * 1e3, "gen_tokens_per_s": B * G / t_smp,
-            "vs_greedy_gen": (t_pre + t_dec) / t_smp,
-            "top_p_0.9_gen_ms": t_topp * 1e3, "top_p_vs_greedy_gen": (t_pre + t_dec) / t_topp,
-            "lmhead_us_sampled_logprobs": lm_s.total_ms / lm_s.launches * 1e3 if lm_s.launches else None,
-            "lmhead_us_greedy": kern["lmhead"]["avg_us"] if "lmhead" in kern else None,
-            "mean_logprob": float(lps.mean()), "logprobs_finite": bool((lps == lps).all())}
-        log(f"sampled: {json.dumps(res['sampled'])}")
+        if not args.no_extras:
+            # sampled generation (temperature 0.7, Gumbel-max with Philox4x64-10) with per-token
+            # log-probabilities, same shape and fused weights: whole-generation time beside the
+            # greedy one, and the LM head's time per launch in each mode
+            with torch.cuda.stream(st):
+                lpb = torch.empty(B, G, dtype=torch.float32, device="cuda")
+                smp = he.he_sampling(0.7, 1234)
+                E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                he.he_fuse_lora(ctx, lt)
+                he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp, out.data_ptr(), lpb.data_ptr())  # graph capture
+                E[0].record(st)
+                he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp, out.data_ptr(), lpb.data_ptr())
+                E[1].record(st)
+                # the same with a top-p 0.9 nucleus (graph captured by the first call)
+                smp_p = he.he_sampling(0.7, 1234, 0.9)
+                Ep = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp_p, out.data_ptr(), lpb.data_ptr())
+                Ep[0].record(st)
+                he.he_generate_ex(ctx, prompts.data_ptr(), B, S, G, smp_p, out.data_ptr(), lpb.data_ptr())
+                Ep[1].record(st)
+                he.he_kernel_timer(ctx, he.HE_K_LMHEAD, True)
+                he.he_generate_ex(ctx, prompts.data_ptr(), B, S, 8, smp, out.data_ptr(), lpb.data_ptr())
+                lm_s = he.he_kernel_stats(ctx, he.HE_K_LMHEAD)
+                he.he_kernel_timer(ctx, he.HE_K_LMHEAD, False)
+                he.he_unfuse_lora(ctx, lt)
+                he.he_sync(ctx)
+                torch.cuda.synchronize()
+            t_smp = E[0].elapsed_time(E[1]) / 1e3
+            t_topp = Ep[0].elapsed_time(Ep[1]) / 1e3
+            lps = lpb.cpu().numpy()
+            res["sampled"] = {
+                "temperature": 0.7, "gen_ms": t_smp * 1e3, "gen_tokens_per_s": B * G / t_smp,
+                "vs_greedy_gen": (t_pre + t_dec) / t_smp,
+                "top_p_0.9_gen_ms": t_topp * 1e3, "top_p_vs_greedy_gen": (t_pre + t_dec) / t_topp,
+                "lmhead_us_sampled_logprobs": lm_s.total_ms / lm_s.launches * 1e3 if lm_s.launches else None,
+                "lmhead_us_greedy": kern["lmhead"]["avg_us"] if "lmhead" in kern else None,
+                "mean_logprob": float(lps.mean()), "logprobs_finite": bool((lps == lps).all())}
+            log(f"sampled: {json.dumps(res['sampled'])}")
 
-        # weight-only FP8 decode (a separate mode: E4M3 projection weights, half the
-        # weight bytes per step): greedy generation beside the bf16 one, and the decode
-        # GEMVs' time per launch with their algorithmic (one byte per weight) traffic
-        with torch.cuda.stream(st):
-            he.he_fuse_lora(ctx, lt)
-            he.he_set_fp8_decode(ctx, True)
-            Ef = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            he.he_generate(ctx, prompts.data_ptr(), B, S, G, out.data_ptr())     # graph capture
-            Ef[0].record(st)
-            he.he_generate(ctx, prompts.data_ptr(), B, S, G, out.data_ptr())
-            Ef[1].record(st)
-            he.he_kernel_timer(ctx, he.HE_K_GEMV_DECODE, True)
-            he.he_generate(ctx, prompts.data_ptr(), B, S, 8, out.data_ptr())
-            gv8 = he.he_kernel_stats(ctx, he.HE_K_GEMV_DECODE)
-            he.he_kernel_timer(ctx, he.HE_K_GEMV_DECODE, False)
-            he.he_set_fp8_decode(ctx, False)
-            he.he_unfuse_lora(ctx, lt)
-            he.he_sync(ctx)
-            torch.cuda.synchronize()
-        t_f8 = Ef[0].elapsed_time(Ef[1]) / 1e3
-        L_, d_, F_ = a.n_layers, a.d_model, a.d_ffn
-        w_bf16 = L_ * (4 * d_ * d_ + 2 * d_ * F_) * 2
-        w_f8 = L_ * ((4 * d_ * d_ + 2 * d_ * F_) + 4 * (5 * d_ + F_))     # codes + per-row scales
-        f8_step_bytes = dec_bytes / (G - 1) - w_bf16 + w_f8
-        res["fp8_decode"] = {
-            "gen_ms": t_f8 * 1e3, "gen_tokens_per_s": B * G / t_f8, "vs_bf16_gen": (t_pre + t_dec) / t_f8,
-            "decode_ms_est": t_f8 * 1e3 - t_pre * 1e3,
-            "decode_bytes_per_step_avg": f8_step_bytes,
-            "decode_hbm_GBps_est": f8_step_bytes * (G - 1) / (t_f8 - t_pre) / 1e9,
-            "gemv_avg_us": gv8.total_ms / gv8.launches * 1e3 if gv8.launches else None,
-            "gemv_GBps": gv8.bytes / (gv8.total_ms / 1e3) / 1e9 if gv8.total_ms else None}
-        log(f"fp8_decode: {json.dumps(res['fp8_decode'])}")
+            # weight-only FP8 decode (a separate mode: E4M3 projection weights, half the
+            # weight bytes per step): greedy generation beside the bf16 one, and the decode
+            # GEMVs' time per launch with their algorithmic (one byte per weight) traffic
+            with torch.cuda.stream(st):
+                he.he_fuse_lora(ctx, lt)
+                he.he_set_fp8_decode(ctx, True)
+                Ef = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                he.he_generate(ctx, prompts.data_ptr(), B, S, G, out.data_ptr())     # graph capture
+                Ef[0].record(st)
+                he.he_generate(ctx, prompts.data_ptr(), B, S, G, out.data_ptr())
+                Ef[1].record(st)
+                he.he_kernel_timer(ctx, he.HE_K_GEMV_DECODE, True)
+                he.he_generate(ctx, prompts.data_ptr(), B, S, 8, out.data_ptr())
+                gv8 = he.he_kernel_stats(ctx, he.HE_K_GEMV_DECODE)
+                he.he_kernel_timer(ctx, he.HE_K_GEMV_DECODE, False)
+                he.he_set_fp8_decode(ctx, False)
+                he.he_unfuse_lora(ctx, lt)
+                he.he_sync(ctx)
+                torch.cuda.synchronize()
+            t_f8 = Ef[0].elapsed_time(Ef[1]) / 1e3
+            L_, d_, F_ = a.n_layers, a.d_model, a.d_ffn
+            w_bf16 = L_ * (4 * d_ * d_ + 2 * d_ * F_) * 2
+            w_f8 = L_ * ((4 * d_ * d_ + 2 * d_ * F_) + 4 * (5 * d_ + F_))     # codes + per-row scales
+            f8_step_bytes = dec_bytes / (G - 1) - w_bf16 + w_f8
+            res["fp8_decode"] = {
+                "gen_ms": t_f8 * 1e3, "gen_tokens_per_s": B * G / t_f8, "vs_bf16_gen": (t_pre + t_dec) / t_f8,
+                "decode_ms_est": t_f8 * 1e3 - t_pre * 1e3,
+                "decode_bytes_per_step_avg": f8_step_bytes,
+                "decode_hbm_GBps_est": f8_step_bytes * (G - 1) / (t_f8 - t_pre) / 1e9,
+                "gemv_avg_us": gv8.total_ms / gv8.launches * 1e3 if gv8.launches else None,
+                "gemv_GBps": gv8.bytes / (gv8.total_ms / 1e3) / 1e9 if gv8.total_ms else None}
+            log(f"fp8_decode: {json.dumps(res['fp8_decode'])}")
 
-        # teacher-forced scoring of the finished experience (prompt + the answer just
-        # sampled, S + G tokens): log-probabilities of the B x G answer tokens, fused weights
-        with torch.cuda.stream(st):
-            seq = torch.cat([prompts, out], dim=1).contiguous()
-            lpt = torch.empty(B, G, dtype=torch.float32, device="cuda")
-            E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            he.he_fuse_lora(ctx, lt)
-            he.he_logprobs(ctx, seq.data_ptr(), B, S + G, S, lpt.data_ptr())
-            E[0].record(st)
-            for _ in range(2):
+            # teacher-forced scoring of the finished experience (prompt + the answer just
+            # sampled, S + G tokens): log-probabilities of the B x G answer tokens, fused weights
+            with torch.cuda.stream(st):
+                seq = torch.cat([prompts, out], dim=1).contiguous()
+                lpt = torch.empty(B, G, dtype=torch.float32, device="cuda")
+                E = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                he.he_fuse_lora(ctx, lt)
                 he.he_logprobs(ctx, seq.data_ptr(), B, S + G, S, lpt.data_ptr())
-            E[1].record(st)
-            cls = {"gemm": he.HE_K_GEMM_PREFILL, "attn": he.HE_K_ATTN_PREFILL, "vocab": he.HE_K_VOCAB}
-            for k in cls.values():
-                he.he_kernel_timer(ctx, k, True)
-            he.he_logprobs(ctx, seq.data_ptr(), B, S + G, S, lpt.data_ptr())
-            cs = {n: he.he_kernel_stats(ctx, k) for n, k in cls.items()}
-            for k in cls.values():
-                he.he_kernel_timer(ctx, k, False)
-            he.he_unfuse_lora(ctx, lt)
-            he.he_sync(ctx)
-            torch.cuda.synchronize()
-        t_sc = E[0].elapsed_time(E[1]) / 1e3 / 2
-        T = S + G
-        L, d, F, V = a.n_layers, a.d_model, a.d_ffn, a.vocab
-        sc_flops = (2.0 * B * T * L * (4 * d * d + 2 * d * F) + 2.0 * L * d * T * (T + 1) * B
-                    + 2.0 * B * G * d * V)
-        lpv = lpt.cpu().numpy()
-        tf = lambda st_: st_.flops / (st_.total_ms / 1e3) / 1e12 if st_.total_ms else None
-        res["scoring"] = {
-            "sequence": T, "prompt_len": S, "answer_len": G, "ms": t_sc * 1e3,
-            "scored_tokens_per_s": B * G / t_sc, "TFLOPs": sc_flops / t_sc / 1e12,
-            "mfma_frac": sc_flops / t_sc / BF16_PEAK,
-            "layer_gemm_ms": cs["gemm"].total_ms, "layer_gemm_TFLOPs": tf(cs["gemm"]),
-            "attn_ms": cs["attn"].total_ms,
-            "vocab_ms": cs["vocab"].total_ms, "vocab_TFLOPs": tf(cs["vocab"]),
-            "mean_logprob": float(lpv.mean()), "logprobs_finite": bool(((lpv == lpv) & (abs(lpv) < float("inf"))).all())}
-        log(f"scoring: {json.dumps(res['scoring'])}")
+                E[0].record(st)
+                for _ in range(2):
+                    he.he_logprobs(ctx, seq.data_ptr(), B, S + G, S, lpt.data_ptr())
+                E[1].record(st)
+                cls = {"gemm": he.HE_K_GEMM_PREFILL, "attn": he.HE_K_ATTN_PREFILL, "vocab": he.HE_K_VOCAB}
+                for k in cls.values():
+                    he.he_kernel_timer(ctx, k, True)
+                he.he_logprobs(ctx, seq.data_ptr(), B, S + G, S, lpt.data_ptr())
+                cs = {n: he.he_kernel_stats(ctx, k) for n, k in cls.items()}
+                for k in cls.values():
+                    he.he_kernel_timer(ctx, k, False)
+                he.he_unfuse_lora(ctx, lt)
+                he.he_sync(ctx)
+                torch.cuda.synchronize()
+            t_sc = E[0].elapsed_time(E[1]) / 1e3 / 2
+            T = S + G
+            L, d, F, V = a.n_layers, a.d_model, a.d_ffn, a.vocab
+            sc_flops = (2.0 * B * T * L * (4 * d * d + 2 * d * F) + 2.0 * L * d * T * (T + 1) * B
+                        + 2.0 * B * G * d * V)
+            lpv = lpt.cpu().numpy()
+            tf = lambda st_: st_.flops / (st_.total_ms / 1e3) / 1e12 if st_.total_ms else None
+            res["scoring"] = {
+                "sequence": T, "prompt_len": S, "answer_len": G, "ms": t_sc * 1e3,
+                "scored_tokens_per_s": B * G / t_sc, "TFLOPs": sc_flops / t_sc / 1e12,
+                "mfma_frac": sc_flops / t_sc / BF16_PEAK,
+                "layer_gemm_ms": cs["gemm"].total_ms, "layer_gemm_TFLOPs": tf(cs["gemm"]),
+                "attn_ms": cs["attn"].total_ms,
+                "vocab_ms": cs["vocab"].total_ms, "vocab_TFLOPs": tf(cs["vocab"]),
+                "mean_logprob": float(lpv.mean()), "logprobs_finite": bool(((lpv == lpv) & (abs(lpv) < float("inf"))).all())}
+            log(f"scoring: {json.dumps(res['scoring'])}")
 
     with torch.cuda.stream(st):
         he.he_release_cache(ctx)
         he.he_sync(ctx)
     eng.close()
 
-    if not args.no_breakdown and not args.no_graph:
+    if wl.rounds == 2 and not args.no_breakdown:
+        res["sequence"] = two_round_sequence(wl, a, dev, ldev, prompts, args.seed)
+        log(f"sequence: {json.dumps(res['sequence'])}")
+
+    if not args.no_breakdown and not args.no_graph and not args.no_extras:
         # the same decode phase launched directly (no hipGraph replay), for the graph gain
         eng2 = he.Engine(a, dev, use_graph=False)
         ctx2, st2 = eng2.ctx, eng2.stream
@@ -615,7 +695,7 @@ def main():
         res["phases"]["graph_speedup"] = t_dec_direct / (res["phases"]["decode_ms"] / 1e3)
         log(f"decode without graph: {t_dec_direct * 1e3:.1f} ms (graph gain x{res['phases']['graph_speedup']:.3f})")
 
-    if not args.no_breakdown:
+    if not args.no_breakdown and not args.no_extras:
         # reward scoring (the largest workload's OPT-350m-shape reward model, post-LN, its own
         # shape): 128 sequences x 512 tokens, one full causal pass plus the scalar head
         rw = synth.WORKLOADS["opt13b"]

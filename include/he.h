@@ -96,7 +96,10 @@ enum {
  *              inference_tp_size); only 1 is implemented (HE_E_UNSUPPORTED).
  *   use_graph: replay the decode step from a captured hipGraph (page 2,
  *              section 4, enable_cuda_graph).  The environment variable
- *              HE_NO_GRAPH=1 turns it off.
+ *              HE_NO_GRAPH=1 turns it off.  HE_DEBUG=1 (read at he_create) turns
+ *              it off too and makes every call wait for the stream after each
+ *              kernel launch and check for an error; the first failure is
+ *              returned as HE_E_HIP with the kernel named in he_last_error.
  *   flags:     HE_FLAG_* bits.
  */
 typedef struct he_model_desc {

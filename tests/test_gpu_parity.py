@@ -261,3 +261,34 @@ def test_opt125m_ragged_prompt_pass(c2_inputs):
     full = om.forward_full(seq)
     for j in range(3):
         check_logits(got[j], full[:, S - 1 + j], C2.actor, f"ragged step {j}")
+
+
+def test_opt125m_debug_mode_waits_after_every_launch(c2_inputs, monkeypatch):
+    """HE_DEBUG=1 (read at he_create): every launch is followed by a stream wait and an
+    error check, graph replay is off.  A generation, a teacher-forced step with logits
+    and a scoring pass then give the same bits as the ordinary graph-replayed run."""
+    params, lora, prompts, forced = c2_inputs
+    B, S, G = C2.batch, C2.prompt_len, 12
+    outs = {}
+    for mode in ("normal", "debug"):
+        if mode == "debug":
+            monkeypatch.setenv("HE_DEBUG", "1")
+        run = GpuRun(C2, params)
+        monkeypatch.delenv("HE_DEBUG", raising=False)
+        lt = run.lora(lora)
+        with torch.cuda.stream(run.stream):
+            he.he_fuse_lora(run.ctx, lt)
+            he.he_retake_cache(run.ctx, B, C2.max_seq)
+        gen = run.generate(prompts, G)
+        lg = run.teacher_forced(prompts, forced, 3, want_steps={2})[2]
+        seq = torch.cat([prompts, forced[:, :8]], dim=1).to(torch.int32).cuda()
+        lp = torch.empty(B, 8, dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(run.stream):
+            he.he_logprobs(run.ctx, seq.data_ptr(), B, S + 8, S, lp.data_ptr())
+            he.he_sync(run.ctx)
+        outs[mode] = (gen, lg, lp.cpu().numpy())
+        run.close()
+    log("debug mode: generation, logits and log-probabilities compared bit for bit")
+    assert np.array_equal(outs["normal"][0], outs["debug"][0])
+    assert np.array_equal(outs["normal"][1].view(np.uint32), outs["debug"][1].view(np.uint32))
+    assert np.array_equal(outs["normal"][2].view(np.uint32), outs["debug"][2].view(np.uint32))

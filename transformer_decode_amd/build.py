@@ -47,6 +47,53 @@ def _compile(src: str) -> str:
     return obj
 
 
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libhe_asan.so")
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime of the ROCm clang (to preload into a host process)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        hits = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        if not hits:
+            raise RuntimeError("AddressSanitizer runtime not found")
+        path = hits[0]
+    return path
+
+
+def build_asan(verbose: bool = True) -> str:
+    """libhe with the host runtime (he_api.cpp) built under AddressSanitizer, for the
+    host-side tests (HE_FLAG_VALIDATE_ONLY).  The sanitizer applies to host code only
+    (each -fsanitize sits after -Xarch_host); the kernels are the normal build's objects."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    heads = [os.path.join(CSRC, h) for h in ("common.h", "kernels.h")] + [os.path.join(INCLUDE, "he.h")]
+    newest_head = max(os.path.getmtime(h) for h in heads)
+    for s in SOURCES:                     # the kernels' objects of the normal build, made if stale
+        o = os.path.join(BUILD, s + ".o")
+        if s != "he_api.cpp" and (not os.path.exists(o) or os.path.getmtime(o) <
+                                  max(newest_head, os.path.getmtime(os.path.join(CSRC, s)))):
+            os.makedirs(BUILD, exist_ok=True)
+            _compile(s)
+    obj = os.path.join(ASAN_DIR, "he_api.cpp.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *san, "-c", os.path.join(CSRC, "he_api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling he_api.cpp with ASan failed:\n{' '.join(cmd)}\n{r.stderr}")
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s != "he_api.cpp"] + [obj]
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+           "-shared-libasan", *objs, "-o", ASAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"linking the ASan library failed:\n{' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:

@@ -60,6 +60,7 @@ struct he_ctx {
   int dt = DT_BF16, L = 0, d = 0, H = 0, D = 0, F = 0, V = 0, de = 0;
   float q_scale = 1.f;
   bool validate_only = false, use_graph = true;
+  bool debug = false;             // HE_DEBUG=1: synchronise and check after every launch
   bool fused = false, failed = false;
   int il_d = 0;                   // inference layout of the K = d weights (bf16)
   std::string err;
@@ -157,12 +158,30 @@ static he_status hip_fail(he_ctx* c, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail((c), e_, #call); \
   } while (0)
 
-// After a batch of launches: surface launch errors.
+// After a batch of launches: surface launch errors (and a failure HE_DEBUG found).
 static he_status check_launch(he_ctx* c, const char* what) {
+  if (c->failed) return HE_E_HIP;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(c, e, what);
   return HE_OK;
 }
+
+// HE_DEBUG=1: after a launch, wait for the stream and check for an error, so that a
+// fault is reported at the kernel that caused it ("<what>: <error>" in he_last_error).
+// Nothing happens during graph capture (debug mode turns graph replay off) or after a
+// first failure.
+static void dbg_after(he_ctx* c, const char* what) {
+  if (!c->debug || c->capturing || c->failed || c->validate_only) return;
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) hip_fail(c, e, what);
+}
+
+static const char* const kClassName[HE_K_COUNT] = {"LoRA fold", "embedding / LayerNorm", "prompt-pass GEMM",
+                                                   "prompt-pass attention", "decode projection",
+                                                   "decode attention", "LM head", "reward head",
+                                                   "vocabulary GEMM"};
 
 static void* kcache(he_ctx* c, int l) {
   return (char*)c->kv + (size_t)(2 * l) * c->kv_layer_elems * esize(c->dt);
@@ -173,7 +192,18 @@ static void* vcache(he_ctx* c, int l) {
 
 // Run one launch, bracketed by events when its kernel class is armed.
 template <class Fn>
+static void run_k_timed(he_ctx* c, int kclass, double bytes, double flops, Fn&& fn);
+
+// Run one launch of a kernel class (timed when the class is armed; checked right
+// after under HE_DEBUG).
+template <class Fn>
 static void run_k(he_ctx* c, int kclass, double bytes, double flops, Fn&& fn) {
+  run_k_timed(c, kclass, bytes, flops, fn);
+  dbg_after(c, kClassName[kclass]);
+}
+
+template <class Fn>
+static void run_k_timed(he_ctx* c, int kclass, double bytes, double flops, Fn&& fn) {
   Timer& t = c->timers[kclass];
   if (!t.armed || c->capturing) {
     fn();
@@ -325,6 +355,7 @@ static void enqueue_lm_head(he_ctx* c, int B, bool want_logits) {
   else
     launch_argmax_finalize(c->best_val, c->best_idx, smp, c->n_argmax_blocks, B, c->ids_cur, c->tokens,
                            c->want_logp ? c->logp : nullptr, c->max_seq + 1, c->pos_next, c->pos_dev, nullptr, st);
+  dbg_after(c, nucleus ? "top-p pick" : "pick finalisation");
 }
 
 // Decoder layers of the prompt pass of a pre-LN LM-head model over ids [B, S]: leaves
@@ -482,6 +513,7 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
   const int ald = a_il(c, d), alf = a_il(c, F), x0 = c->L ? -ald : 0;
   if (de != d) {
     launch_embed_gather(dt, ids, c->wt.tok_emb, c->xe, M, de, c->V, st);
+    dbg_after(c, "embedding gather");
     EpiArgs e;
     e.mode = EPI_POSADD; e.pos_emb = c->wt.pos_emb; e.h = c->h; e.out = c->x; e.seq_len = S; e.pos0 = 0;
     e.o_il = (post || !c->L) ? -x0 : 0;   // pre-LN: the norm below writes the GEMM input
@@ -490,11 +522,13 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
     if (!post && c->L)
       launch_norm(dt, c->h, nullptr, 0, nullptr, c->layers[0].ln1_g, c->layers[0].ln1_b, eps, c->x, M, d,
                   1, 0, 0, x0, st);
+    dbg_after(c, "LayerNorm");
   } else {
     launch_embed_norm(dt, ids, nullptr, S, c->wt.tok_emb, c->wt.pos_emb,
                       (!post && c->L) ? c->layers[0].ln1_g : nullptr,
                       (!post && c->L) ? c->layers[0].ln1_b : nullptr, eps, c->h, c->x, M, d, c->V,
                       e_il(c), x0, st);
+    dbg_after(c, "embedding / LayerNorm");
   }
   const int ild = w_il(c, d), ilf = w_il(c, F);
   for (int l = 0; l < c->L; ++l) {
@@ -541,6 +575,7 @@ static void enqueue_score(he_ctx* c, const int32_t* ids, int B, int S, float* re
   int xs = S;
   if (!post) {   // pre-LN: final LayerNorm of the last position
     launch_norm(dt, c->h, nullptr, 0, nullptr, c->wt.lnf_g, c->wt.lnf_b, eps, c->x, B, d, S, S - 1, 0, 0, st);
+    dbg_after(c, "final LayerNorm");
     xs = 1;
   }
   run_k(c, HE_K_SCORE, (double)de * d * es, 2.0 * B * de * d,
@@ -618,6 +653,8 @@ he_status he_create(const he_model_desc* desc, const he_weight_table* w, void* h
   c->validate_only = (D.flags & HE_FLAG_VALIDATE_ONLY) != 0;
   const char* ng = std::getenv("HE_NO_GRAPH");
   c->use_graph = D.use_graph && !(ng && ng[0] == '1');
+  const char* dbg = std::getenv("HE_DEBUG");
+  c->debug = dbg && dbg[0] == '1';
   if (!c->validate_only) {
     if (hipGetDevice(&c->device) != hipSuccess) {
       delete c;
@@ -687,6 +724,7 @@ static he_status f8_requantize(he_ctx* c) {
     launch_quantize_fp8(w.w_out, d, d, w_il(c, d), c->f8[l].q[1], c->f8[l].s[1], c->stream);
     launch_quantize_fp8(w.w_fc1, F, d, w_il(c, d), c->f8[l].q[2], c->f8[l].s[2], c->stream);
     launch_quantize_fp8(w.w_fc2, d, F, w_il(c, F), c->f8[l].q[3], c->f8[l].s[3], c->stream);
+    dbg_after(c, "FP8 quantisation");
   }
   return check_launch(c, "fp8 quantisation launch");
 }
@@ -755,6 +793,7 @@ he_status he_fp8_export(he_ctx* c, int32_t layer, int32_t proj, uint8_t* d_codes
   const int d = c->d, F = c->F;
   const int N[4] = {3 * d, d, F, d}, K[4] = {d, d, d, F};
   launch_fp8_rowmajor(c->f8[layer].q[proj], N[proj], K[proj], d_codes, c->stream);
+  dbg_after(c, "FP8 export");
   HIP_TRY(c, hipMemcpyAsync(d_scales, c->f8[layer].s[proj], (size_t)N[proj] * 4, hipMemcpyDeviceToDevice,
                             c->stream));
   return check_launch(c, "fp8 export launch");
@@ -944,6 +983,7 @@ static he_status prefill_checks(he_ctx* c, const int32_t* ids, int B, int S, con
 static he_status do_prefill(he_ctx* c, const int32_t* ids, int B, int S, bool want_logits) {
   set_plans(c, B);
   launch_set_i32(c->pos_dev, S - 1, c->stream);
+  dbg_after(c, "position set");
   enqueue_prefill_lm(c, ids, B, S, want_logits);
   he_status s = check_launch(c, "prefill launch");
   if (s != HE_OK) return s;
@@ -988,7 +1028,7 @@ static he_status run_step(he_ctx* c, bool want_logits) {
     return set_err(c, HE_E_HIP, "injected device fault");
   }
   const int B = c->cur_B;
-  const bool graph = c->use_graph && !any_timer_armed(c);
+  const bool graph = c->use_graph && !any_timer_armed(c) && !c->debug;
   if (graph) {
     hipGraphExec_t& ge = c->graph[want_logits ? 1 : 0];
     if (c->graph_B != B || c->graph_fused != c->fused || c->graph_itemp != c->inv_temp ||
@@ -1180,6 +1220,7 @@ static he_status enqueue_sample(he_ctx* c, const float* d_logits, int32_t B, int
     launch_argmax_finalize(ps.best_val, ps.best_idx, smpa, nb, B, nullptr, d_tokens,
                            want_lp ? d_logprobs : nullptr, 0, ps.spos + 1, nullptr, nullptr, st);
   }
+  dbg_after(c, "sample");
   return check_launch(c, "sample launch");
 }
 
@@ -1235,6 +1276,7 @@ static void enqueue_logprobs(he_ctx* c, const int32_t* seq, int B, int S, int S_
         launch_gemm(dt, xr, c->wt.tok_emb, mc, c->V, d, e, st);
       }
       launch_logprob_gather(c->lgc, mc, c->V, seq, S, S_p, n, r0, out, st);
+      dbg_after(c, "log-probability gather");
     });
   }
 }

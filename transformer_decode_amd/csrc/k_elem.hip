@@ -466,11 +466,105 @@ __global__ __launch_bounds__(256, NC <= 16 ? 4 : 3) void norm_rows_kernel(float*
   }
 }
 
+// LayerNorm of the rows of one 16-row block of the inference layout (bf16 GEMM input,
+// x_lay < 0), one wave per row.  In that layout the block's rows keep their 16 row
+// segments in memory and only the 16-byte units inside each block of 16 rows x BW
+// columns move, so a column chunk of whole blocks is 16 contiguous row pieces.  The
+// rounded outputs of one chunk are staged in LDS row-major (rows padded by 16 bytes,
+// so the gathers below hit distinct banks), then each thread fetches the unit that
+// belongs at its place of the chunk's memory and writes it: every HBM line is written
+// whole, where one wave per row would write 8 bytes into each of 64 lines.
+constexpr int kNbCols = 2048;     // columns per staged chunk (16 x 2056 bf16, 64.25 KB)
+template <int NC>
+__global__ __launch_bounds__(1024) void norm_block_kernel(float* __restrict__ h, const bf16* __restrict__ g,
+                                                          const bf16* __restrict__ b, float eps,
+                                                          bf16* __restrict__ x, int M, int d, int row_stride,
+                                                          int row_offset, int post, int il, int row_group) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[16 * (kNbCols + 8)];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
+  const int r0 = blockIdx.x * 16, r = r0 + w;
+  const bool live = r < M;
+  const size_t row = live ? (size_t)(r / row_group) * row_stride + row_offset + r % row_group : 0;
+  float* hr = h + row * d;
+  const int nch = d / 4;
+  float v[NC][4];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = lane + c * kWave;
+    if (live && ch < nch) {                      // the stream row is read once here
+      const uint4 u = ld_once(hr + ch * 4);
+      v[c][0] = __uint_as_float(u.x); v[c][1] = __uint_as_float(u.y);
+      v[c][2] = __uint_as_float(u.z); v[c][3] = __uint_as_float(u.w);
+    } else {
+      v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.f;
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += v[c][q];
+  const float mean = wave_sum(s) / (float)d;
+  float s2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (lane + c * kWave < nch)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { const float t = v[c][q] - mean; s2 += t * t; }
+  const float var = wave_sum(s2) / (float)d;
+  const float rstd = 1.f / sqrtf(var + eps);
+  const int lgu = il - 3, umask = (1 << lgu) - 1;   // 16-byte units per block row
+  constexpr int TS = kNbCols + 8;                  // staged row stride (elements)
+  for (int c0 = 0; c0 < d; c0 += kNbCols) {
+    const int cw = min(kNbCols, d - c0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int k = (lane + c * kWave) * 4;
+      if (live && k < d && k >= c0 && k < c0 + cw) {
+        float gv[4], bv[4], y[4];
+        ld4(g + k, gv);
+        ld4(b + k, bv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[q] = (v[c][q] - mean) * rstd * gv[q] + bv[q];
+        if (post) st4(hr + k, y);                  // post-LN: the stream is the norm
+        st4(tile + w * TS + (k - c0), y);
+      }
+    }
+    __syncthreads();
+    // memory unit (block row sr, unit column sc / 8 of the chunk) holds, by il_off, unit
+    // (row j, unit column u) of its block with position p = (u / 4) 64 + (u % 4) 16 + j.
+    // A block's rows are spread over all 16 of its memory rows, so a block that is only
+    // partly filled (M % 16 != 0) writes the units of its live rows, wherever they lie
+    // (the buffer holds whole 16-row blocks).
+    const int per_row = cw / 8;
+    for (int i = threadIdx.x; i < 16 * per_row; i += 1024) {
+      const int sr = i / per_row, sc = (i - sr * per_row) * 8;
+      const int ub = sc >> il << il;                     // the layout block's first column in the chunk
+      const int p = (sr << lgu) | ((sc >> 3) & umask);   // position inside that block
+      const int j = p & 15, u = ((p >> 6) << 2) | ((p >> 4) & 3);
+      if (r0 + j < M)
+        *reinterpret_cast<uint4*>(x + (size_t)(r0 + sr) * d + c0 + sc) =
+            *reinterpret_cast<const uint4*>(tile + j * TS + ub + u * 8);
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T>
 static bool launch_norm_rows(float* h, const T* g, const T* b, float eps, T* x, int M, int d,
                              int row_stride, int row_offset, int post, int x_lay, int row_group,
                              hipStream_t st) {
   const int per_lane = (d / 4 + kWave - 1) / kWave;
+  if constexpr (sizeof(T) == 2) {
+    // rows of up to 1024 into the inference layout: 16-row blocks staged through LDS
+    // (measured at 16384 rows: d = 1024 31.2 -> 21.8 us; at d = 4096 one WG per CU
+    // serialises load, staging and stores and loses, 104.7 -> 114.1 us)
+    if (x_lay < 0 && per_lane <= 4) {
+      norm_block_kernel<4><<<(M + 15) / 16, 1024, 0, st>>>(h, (const bf16*)g, (const bf16*)b, eps, (bf16*)x,
+                                                            M, d, row_stride, row_offset, post, -x_lay, row_group);
+      return true;
+    }
+  }
   const dim3 grid((M + 3) / 4), block(256);
 #define HE_NORM_ROWS(NC)                                                                          \
   norm_rows_kernel<T, NC><<<grid, block, 0, st>>>(h, g, b, eps, x, M, d, row_stride, row_offset, \

@@ -11,7 +11,9 @@ import os
 from typing import Dict, Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhe.so")
+# HE_LIB names another build of the same library (the host-side AddressSanitizer
+# build of the CPU tests); by default the in-tree libhe.so
+LIB_PATH = os.environ.get("HE_LIB") or os.path.join(_PKG, "libhe.so")
 
 # status codes
 HE_OK, HE_E_ARG, HE_E_STATE, HE_E_NOCACHE, HE_E_RANGE, HE_E_OOM, HE_E_HIP, HE_E_UNSUPPORTED = (
