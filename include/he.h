@@ -288,6 +288,18 @@ he_status he_generate_ex(he_ctx* ctx, const int32_t* d_prompt, int32_t B, int32_
 he_status he_sample(he_ctx* ctx, const float* d_logits, int32_t B, int32_t position,
                     const he_sampling* smp, int32_t* d_tokens, float* d_logprobs);
 
+/* he_sample for callers that cannot allocate device memory (work under graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same rule, arguments,
+ * outputs and errors, but it needs no workspace (no he_retake_cache, no HE_E_NOCACHE)
+ * and allocates nothing.  Its per-block partials live in a static device array of
+ * 1.25 MB (plus 256 bytes) that each GPU the library runs on holds until the process
+ * ends; every call on one GPU uses that GPU's array, so calls that overlap on one GPU
+ * (other streams, other contexts, other threads) race: order them on one stream.
+ * Limits: B * ceil(vocab / 128) <= 65536 (B <= 128 at vocab <= 65536), else HE_E_ARG;
+ * vocab <= 65536, else HE_E_UNSUPPORTED. */
+he_status he_sample_static(he_ctx* ctx, const float* d_logits, int32_t B, int32_t position,
+                           const he_sampling* smp, int32_t* d_tokens, float* d_logprobs);
+
 /* Reward scoring (page 1, pipeline section: the reward model gives each response
  * a scalar score): full causal pass over d_ids [B, S] of a HE_HEAD_SCALAR model,
  * d_reward [B] float32 = y . score_w with y = h[S-1] proj_out^T (h[S-1] itself when

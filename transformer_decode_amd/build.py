@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhe.so")
 
 ARCH = "gfx950"
-SOURCES = ["k_elem.hip", "k_gemm.hip", "k_gemv.hip", "k_attn.hip", "k_fp8.hip", "he_api.cpp"]
+SOURCES = ["k_elem.hip", "k_gemm.hip", "k_gemv.hip", "k_attn.hip", "k_fp8.hip", "k_static.hip", "he_api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1238,6 +1238,26 @@ he_status he_sample(he_ctx* c, const float* d_logits, int32_t B, int32_t positio
   return enqueue_sample(c, d_logits, B, position, it, seed, tp, want_lp, ps, d_tokens, d_logprobs);
 }
 
+he_status he_sample_static(he_ctx* c, const float* d_logits, int32_t B, int32_t position,
+                           const he_sampling* smp, int32_t* d_tokens, float* d_logprobs) {
+  if (!c) return HE_E_ARG;
+  const int nb = (c->V + 127) / 128;
+  if (nb > kStaticBlocks)
+    return set_err(c, HE_E_UNSUPPORTED, "vocabulary %d above the static scratch's %d columns", c->V,
+                   kStaticBlocks * 128);
+  float it = 0.f, tp = 1.f;
+  uint64_t seed = 0;
+  bool want_lp = false;
+  he_status s = sample_checks(c, d_logits, B, position, smp, d_tokens, d_logprobs,
+                              kStaticRows * kStaticBlocks / nb, &it, &seed, &tp, &want_lp);
+  if (s != HE_OK || c->validate_only) return s;
+  StaticScratch ss;
+  const hipError_t e = static_scratch(c->device, &ss);
+  if (e != hipSuccess) return hip_fail(c, e, "static scratch address");
+  const PickScratch ps{ss.pos, ss.best_val, ss.best_idx, ss.best_lg, ss.blk_max, ss.blk_sum};
+  return enqueue_sample(c, d_logits, B, position, it, seed, tp, want_lp, ps, d_tokens, d_logprobs);
+}
+
 // Teacher-forced scoring: prompt pass over the whole sequence, final LayerNorm of the
 // positions S_p - 1 .. S - 2 of every row (each predicts the next token), then in
 // chunks of lg_rows rows the tied-head GEMM into fp32 logits and the log-softmax gather.

@@ -231,6 +231,22 @@ void launch_attn_decode_q(int dt, const void* q, const void* k_cache, const void
                           const int32_t* pos_dev, void* o, int B, int H, int D, int S_max,
                           int x_mt, hipStream_t st);
 
+// ---- static scratch of the allocation-free entry point ---------------------------
+// Capacity: rows x 128-column blocks of the pick rule's per-block partials.
+constexpr int kStaticRows = 128, kStaticBlocks = 512;
+struct StaticScratch {
+  int32_t* pos = nullptr;         // [2] position pair (the LM head's pos_dev, pos_next roles)
+  float* best_val = nullptr;      // [kStaticRows * kStaticBlocks] each
+  int32_t* best_idx = nullptr;
+  float* best_lg = nullptr;
+  float* blk_max = nullptr;
+  float* blk_sum = nullptr;
+};
+// The device address of the static scratch on `device` (taken once per device, with
+// that device current, and kept until the process ends).
+hipError_t static_scratch(int device, StaticScratch* out);
+size_t static_scratch_bytes();
+
 // *p = v (a one-thread kernel; safe next to captured work, unlike a memset node)
 void launch_set_i32(int32_t* p, int32_t v, hipStream_t st);
 

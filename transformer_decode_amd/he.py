@@ -82,6 +82,7 @@ _SIGS = {
     "he_generate_ex": (_i32, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
     "he_score": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "he_sample": (_i32, [_vp, _vp, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
+    "he_sample_static": (_i32, [_vp, _vp, _i32, _i32, ctypes.POINTER(he_sampling), _vp, _vp]),
     "he_set_fp8_decode": (_i32, [_vp, _i32]),
     "he_fp8_export": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "he_logprobs": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp]),
@@ -174,6 +175,13 @@ def he_sample(ctx, d_logits: int, B: int, position: int, smp, d_tokens: int, d_l
     """smp: he_sampling or None (greedy)."""
     p = ctypes.byref(smp) if smp is not None else None
     return _check(lib().he_sample(ctx, _vp(d_logits), B, position, p, _vp(d_tokens), _vp(d_logprobs or None)), ctx)
+
+
+def he_sample_static(ctx, d_logits: int, B: int, position: int, smp, d_tokens: int, d_logprobs: int = 0):
+    """he_sample on the library's static device scratch: no workspace, no allocation."""
+    p = ctypes.byref(smp) if smp is not None else None
+    return _check(lib().he_sample_static(ctx, _vp(d_logits), B, position, p, _vp(d_tokens),
+                                         _vp(d_logprobs or None)), ctx)
 
 
 def he_set_fp8_decode(ctx, enable: bool):
