@@ -520,6 +520,53 @@ __global__ __launch_bounds__(512) void gemm_frag_kernel(const bf16* __restrict__
   // 16- or 32-byte access to whole row segments.
   constexpr int PR = 68;
   float* park = reinterpret_cast<float*>(fsm) + (size_t)wv * 32 * PR;
+  if constexpr (MODE == EPI_RESID) {
+    // h += acc + bias: the stream rows of 32-row slice i + 1 are fetched while slice i
+    // is added and stored, so the slices' HBM round trips overlap.  Lane l covers rows
+    // l / 8 + 8 it of a slice and the same 8 columns throughout (one bias load).
+    const int col = (lane & 7) << 3, n = n0 + wn * 64 + col;
+    float bias[8];
+    if (e.bias) load8((const bf16*)e.bias + n, bias);
+    else
+#pragma unroll
+      for (int c = 0; c < 8; ++c) bias[c] = 0.f;
+    auto hrow = [&](int i, int it) { return e.h + (size_t)(m0 + wm * 128 + i * 32 + (lane >> 3) + 8 * it) * N + n; };
+    float hc[4][8], hn[4][8];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) load8(hrow(0, it), hc[it]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(park + rl * PR + j * 32 + q * 8 + ((lane >> 5) << 2)) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      __builtin_amdgcn_s_waitcnt(0xC07F);       // the slice is parked (lgkmcnt(0))
+      if (i < 3)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) load8(hrow(i + 1, it), hn[it]);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = (lane >> 3) + 8 * it;
+        const float4 v0 = *reinterpret_cast<const float4*>(park + row * PR + col);
+        const float4 v1 = *reinterpret_cast<const float4*>(park + row * PR + col + 4);
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        float hv[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) hv[c] = hc[it][c] + (v[c] + bias[c]);
+        store8(hrow(i, it), hv);
+      }
+      // this slice's park reads are done before the next slice parks (stores may fly)
+      __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0), vmcnt and expcnt left open
+      if (i < 3)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) hc[it][c] = hn[it][c];
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
