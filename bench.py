@@ -245,7 +245,9 @@ def two_round_sequence(wl, a, dev, ldev, prompts, seed):
     generation, retake it before the next): round 1 fuse, generate, unfuse, release;
     round 2 retake, fuse, generate, unfuse, release; then the reward model scores the
     round-2 experience (prompt + answer).  Times of each call, the memory the release
-    returns, and whether round 2 repeats round 1's tokens (same adapters)."""
+    returns, and whether round 2 repeats round 1's tokens (same adapters; it may part from
+    them at a near-tie, since the unfold restores each adapted weight to within one bf16
+    spacing and round 2 folds the adapters into those bits)."""
     import torch
 
     import synth
