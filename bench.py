@@ -147,7 +147,7 @@ def kernel_class(name):
         return "attn_prefill"
     if "lora" in name:
         return "lora"
-    if "norm_kernel" in name or "norm_rows" in name or "embed_" in name or "reduce_" in name:
+    if "norm_" in name or "embed_" in name or "reduce_" in name:
         return "embed_norm"
     return "other"
 
