@@ -274,10 +274,11 @@ def test_opt13b_two_rounds_and_reward_scoring():
     Checks: the workspace's memory comes back on release; round 2's logits at rows
     {0, 1, 64, 127}, steps {0, 1, 128, 255} match the oracle; the base weights survive
     both round trips; the rewards of the generated experience are finite and
-    reproducible.  Round 2's tokens are not required to equal round 1's: the unfold
-    returns each adapted weight only to within one bf16 spacing, so round 2 folds the
-    adapters into slightly different bits and its free-running picks may part from
-    round 1's at a near-tie (the agreement is logged)."""
+    reproducible.  Round 2's fold starts from the unfolded weights, which are the
+    originals only to within one bf16 spacing; folding them again reproduces round 1's
+    fused weights except on a few elements in 10^7, each one spacing apart (checked
+    here).  That is enough for free-running picks to part from round 1's at a near-tie,
+    so round 2's tokens are compared with round 1's only as a logged statistic."""
     wl = synth.WORKLOADS["opt13b"]
     a = wl.actor
     B, S, n = wl.batch, wl.prompt_len, wl.gen_len
@@ -290,15 +291,36 @@ def test_opt13b_two_rounds_and_reward_scoring():
     lt = run.lora(lora)
     ws_bytes = 2 * a.n_layers * B * wl.max_seq * a.d_model * 2
     torch.cuda.synchronize()
-    gens, got = [], None
+    gens, got, fused1 = [], None, None
+    wkeys = [k for k in run.dev if k.endswith(".w")]
     for rnd in (1, 2):
+        # free device memory as the library sees it: the test's own transient tensors
+        # are handed back by torch's caching allocator before each reading
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
         free0 = torch.cuda.mem_get_info()[0]
         with torch.cuda.stream(run.stream):
             he.he_retake_cache(run.ctx, B, wl.max_seq)
             he.he_fuse_lora(run.ctx, lt)
             he.he_sync(run.ctx)
         free1 = torch.cuda.mem_get_info()[0]
-        if rnd == 2:
+        if rnd == 1:          # round 1's fused weights, kept in host memory
+            fused1 = {k: run.dev[k].cpu() for k in wkeys}
+        else:                 # compared one matrix at a time on the GPU
+            nd = tot = 0
+            for k in wkeys:
+                ref = fused1.pop(k).cuda()
+                dv = (run.dev[k].view(torch.int16).int() - ref.view(torch.int16).int()).abs()
+                nz = dv[dv != 0]
+                assert (nz == 1).all(), f"{k}: a refolded weight is more than one bf16 spacing from round 1's"
+                nd += int(nz.numel())
+                tot += dv.numel()
+                del ref, dv, nz
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            log(f"opt13b sequence: round 2's fused weights differ from round 1's on {nd} of {tot} elements")
+            assert nd <= 1e-6 * tot
+            free1 = torch.cuda.mem_get_info()[0]
             log("opt13b sequence: round 2 teacher-forced run")
             got = run.teacher_forced(prompts, forced, n, want_rows=rows, want_steps=set(STEPS))
         log(f"opt13b sequence: round {rnd} generation")
@@ -307,6 +329,8 @@ def test_opt13b_two_rounds_and_reward_scoring():
             he.he_unfuse_lora(run.ctx, lt)
             he.he_release_cache(run.ctx)
             he.he_sync(run.ctx)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
         free2 = torch.cuda.mem_get_info()[0]
         log(f"opt13b sequence: round {rnd}: retake took {(free0 - free1) / 1e9:.2f} GB, release returned "
             f"{(free2 - free1) / 1e9:.2f} GB (KV cache {ws_bytes / 1e9:.2f} GB)")
