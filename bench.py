@@ -240,6 +240,59 @@ def stats_summary(stats_csv, workload, command):
     return "\n".join(lines) + "\n"
 
 
+def timeline_summary(trace_csv, workload, command):
+    """The decode steps of a rocprofv3 kernel trace (dispatch start and end on the GPU's
+    clock): each step runs from one step-opening embedding dispatch to the next.  Per
+    step the span, the time inside kernels and the idle gaps between dispatches; per
+    kernel its average duration and the average gap before the next dispatch."""
+    import csv
+    import statistics
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    opens = [i for i, r in enumerate(rows) if "embed_norm" in r["Kernel_Name"]]
+    steps = []
+    for a, b in zip(opens, opens[1:]):
+        names = [rows[i]["Kernel_Name"] for i in range(a, b)]
+        if any("gemv_il" in n for n in names) and not any("gemm_frag" in n for n in names):
+            steps.append((a, b))
+    if steps:   # whole steps only: the interval that spans a generation's end holds other work
+        from collections import Counter
+        common = Counter(b - a for a, b in steps).most_common(1)[0][0]
+        steps = [(a, b) for a, b in steps if b - a == common]
+    per, spans, busy, gaps = {}, [], [], []
+    for a, b in steps:
+        spans.append((int(rows[b]["Start_Timestamp"]) - int(rows[a]["Start_Timestamp"])) / 1e3)
+        k_sum = g_sum = 0.0
+        for i in range(a, b):
+            r = rows[i]
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            gap = (int(rows[i + 1]["Start_Timestamp"]) - int(r["End_Timestamp"])) / 1e3
+            k_sum += dur
+            g_sum += gap
+            gaps.append(gap)
+            e = per.setdefault(r["Kernel_Name"].split("(")[0][:90], [0, 0.0, 0.0])
+            e[0] += 1
+            e[1] += dur
+            e[2] += gap
+        busy.append(k_sum)
+    n = len(steps)
+    lines = [f"# Decode-step dispatch timeline, {workload}", "", "Command (run from the repository root, output "
+             "under gpurun_out/):", "", "```", command, "```", "",
+             f"{n} decode steps of {steps[0][1] - steps[0][0] if steps else 0} dispatches (graph replay). "
+             "Times are the GPU's dispatch start and end stamps; a gap is the time from one dispatch's end "
+             "to the next one's start. A step is one replay of the decode graph; the gap after its last "
+             "dispatch is the time between two graph launches.", "",
+             "| per step | mean | median |", "|---|---|---|",
+             f"| span (us) | {statistics.mean(spans):.1f} | {statistics.median(spans):.1f} |",
+             f"| inside kernels (us) | {statistics.mean(busy):.1f} | {statistics.median(busy):.1f} |",
+             f"| gaps between dispatches (us) | {statistics.mean(spans) - statistics.mean(busy):.1f} | "
+             f"{statistics.median([s - k for s, k in zip(spans, busy)]):.1f} |",
+             f"| gap per dispatch (us) | {statistics.mean(gaps):.2f} | {statistics.median(gaps):.2f} |", "",
+             "| kernel | dispatches per step | avg duration (us) | avg gap after (us) |", "|---|---|---|---|"]
+    for name, (c, d, g) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"| `{name}` | {c / n:.0f} | {d / c:.2f} | {g / c:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def two_round_sequence(wl, a, dev, ldev, prompts, seed):
     """The largest workload's sequence (page 2, section 3: release the workspace after
     generation, retake it before the next): round 1 fuse, generate, unfuse, release;
@@ -338,6 +391,8 @@ def main():
                          "the per-class traffic summary (no GPU)")
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --stats kernel_stats.csv into a markdown summary (no GPU)")
+    ap.add_argument("--timeline-summary", nargs=2, metavar=("TRACE_CSV", "OUT_MD"),
+                    help="write the decode-step dispatch timeline of a rocprofv3 kernel trace")
     ap.add_argument("--mfma-summary", nargs=2, metavar=("MFMA_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --pmc pass of the MFMA counters into a markdown summary (no GPU)")
     ap.add_argument("--command", default="", help="the command that produced the csv (recorded; "
@@ -367,6 +422,16 @@ def main():
             f"python3 bench.py --workload {args.workload} --mfma-summary {m_csv} {o}")
         with open(o, "w") as fh:
             fh.write(mfma_summary(m_csv, args.workload, cmd))
+        return
+    if args.timeline_summary:
+        tr_csv, o = args.timeline_summary
+        cmd = args.command or (
+            f"export TMPDIR=/tmp && "
+            f"timeout -k 10 400 rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof -o bench -- "
+            f"python3 bench.py --workload {args.workload} --steps 1 --warmup 1 --no-cpu --no-breakdown && "
+            f"python3 bench.py --workload {args.workload} --timeline-summary {tr_csv} {o}")
+        with open(o, "w") as fh:
+            fh.write(timeline_summary(tr_csv, args.workload, cmd))
         return
     if args.stats_summary:
         st_csv, o = args.stats_summary
