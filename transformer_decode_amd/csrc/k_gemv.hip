@@ -64,8 +64,8 @@ GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole, 
     // one wave per SIMD).  Measured at the 13B decode shapes, batch 128 (per launch):
     // QKV 58.6 -> 43.1 us, out 24.8 -> 19.3, FC1 77.2 -> 64.0, FC2 88.8 -> 62.6.
     auto rows = [&](int fr) { return (long)(nrb + fr - 1) / fr; };
-    if (whole && rows(2) >= 1024) {        // the LM head: two rows per wave, two waves split K
-      p.fr = 2; p.nwk = K % 256 == 0 ? 2 : 1; p.kr = K / p.nwk; p.splits = 1;
+    if (whole && rows(2) >= 1024) {        // the LM head: 64 rows and the whole K per wave
+      p.fr = 4; p.nwk = 1; p.kr = K; p.splits = 1;   // (batch 128, K 5120: 198.5 -> 135.3 us)
       return p;
     }
     if (whole || N > K) {                  // QKV (fused epilogue) and FC1 (ReLU epilogue): whole K
