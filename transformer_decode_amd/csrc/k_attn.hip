@@ -445,25 +445,47 @@ static int pf_pad(int S, int D, int KV = kPfKV) {
 // K row-major, key-local row `key`, chunk c at chunk c ^ ((key / RPB) mod NCH) of the
 // row; V transposed, row `dim` of Wp keys, chunk j (keys 8 j .. + 8) at chunk
 // j ^ (dim mod 16), each thread transposing an 8 keys x 8 dims block in registers.
-template <int D>
+// Every load of a thread (at most KV / 4096 K chunks and one 8 x 8 V block, Wp D <= KV)
+// is issued before the first LDS write, so staging costs one memory round trip.
+template <int D, int KV>
 __device__ __forceinline__ void pf_stage(const bf16* __restrict__ kc, const bf16* __restrict__ vc,
                                          size_t head, int S, int kw0, int Wp, bf16* Ks, bf16* Vt, int tid) {
-  constexpr int NCH = D / 8, RPB = 128 / D;
-  for (int i = tid; i < Wp * NCH; i += 512) {
-    const int key = i / NCH, c = i - key * NCH;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (kw0 + key < S) v = ld_once(kc + head + (size_t)(kw0 + key) * D + c * 8);
-    *reinterpret_cast<uint4*>(&Ks[key * D + ((c ^ ((key / RPB) & (NCH - 1))) << 3)]) = v;
+  constexpr int NCH = D / 8, RPB = 128 / D, NK = (KV / 8 + 511) / 512;
+  // loads without branches: a slot past the keys reads the head's first row (always
+  // present) and is zeroed where it is written, so the loads issue back to back
+  uint4 kv[NK];
+  uint32_t okm = 0;                                    // bit j: K chunk j, bit NK + r: V row r
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int i = tid + j * 512, key = i / NCH, c = i - key * NCH;
+    const bool ok = i < Wp * NCH && kw0 + key < S;
+    kv[j] = ld_once(kc + head + (ok ? (size_t)(kw0 + key) * D + c * 8 : 0));
+    okm |= (uint32_t)ok << j;
   }
-  for (int i = tid; i < (Wp / 8) * NCH; i += 512) {
-    const int kb = i / NCH, c = i - kb * NCH;
+  const int kb = tid / NCH, cv = tid - kb * NCH;       // this thread's 8 keys x 8 dims of V
+  const bool vblk = tid < (Wp / 8) * NCH;              // (Wp / 8) NCH <= KV / 64 <= 512
+  uint4 vv[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int key = kw0 + kb * 8 + r;
+    const bool ok = vblk && key < S;
+    vv[r] = ld_once(vc + head + (ok ? (size_t)key * D + cv * 8 : 0));
+    okm |= (uint32_t)ok << (NK + r);
+  }
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int i = tid + j * 512, key = i / NCH, c = i - key * NCH;
+    if (i < Wp * NCH)
+      *reinterpret_cast<uint4*>(&Ks[key * D + ((c ^ ((key / RPB) & (NCH - 1))) << 3)]) =
+          (okm >> j) & 1 ? kv[j] : make_uint4(0, 0, 0, 0);
+  }
+  if (vblk) {
     uint32_t e[8][4];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int key = kw0 + kb * 8 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < S) v = ld_once(vc + head + (size_t)key * D + c * 8);
-      e[r][0] = v.x; e[r][1] = v.y; e[r][2] = v.z; e[r][3] = v.w;
+      const bool ok = (okm >> (NK + r)) & 1;
+      e[r][0] = ok ? vv[r].x : 0u; e[r][1] = ok ? vv[r].y : 0u;
+      e[r][2] = ok ? vv[r].z : 0u; e[r][3] = ok ? vv[r].w : 0u;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -472,7 +494,7 @@ __device__ __forceinline__ void pf_stage(const bf16* __restrict__ kc, const bf16
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr)
         w4[pr] = ((e[2 * pr][wd] >> sh) & 0xffffu) | (((e[2 * pr + 1][wd] >> sh) & 0xffffu) << 16);
-      const int dim = c * 8 + j;
+      const int dim = cv * 8 + j;
       *reinterpret_cast<uint4*>(&Vt[dim * Wp + ((kb ^ (dim & 15)) << 3)]) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
   }
@@ -618,7 +640,7 @@ __global__ __launch_bounds__(512, KV < kPfKV ? 4 : 2) void attn_prefill_lds_kern
   const int nqb = (S + 15) / 16;
   const int nqb0 = two ? W / 16 : nqb;          // blocks that finish in the first window
 
-  pf_stage<D>(kc, vc, head, S, 0, S_pad, Ks, Vt, tid);
+  pf_stage<D, KV>(kc, vc, head, S, 0, S_pad, Ks, Vt, tid);
   __syncthreads();
 
   for (int base = 0; base < nqb0; base += 16) {
@@ -651,7 +673,7 @@ __global__ __launch_bounds__(512, KV < kPfKV ? 4 : 2) void attn_prefill_lds_kern
     }
   }
   __syncthreads();                              // every wave done with the first window
-  pf_stage<D>(kc, vc, head, S, W, W, Ks, Vt, tid);
+  pf_stage<D, KV>(kc, vc, head, S, W, W, Ks, Vt, tid);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < ND; ++j) {
