@@ -443,8 +443,11 @@ static int pf_pad(int S, int D, int KV = kPfKV) {
 
 // Stage keys kw0 .. kw0 + Wp - 1 of one head (zeros past S) into the LDS arrays:
 // K row-major, key-local row `key`, chunk c at chunk c ^ ((key / RPB) mod NCH) of the
-// row; V transposed, row `dim` of Wp keys, chunk j (keys 8 j .. + 8) at chunk
-// j ^ (dim mod 16), each thread transposing an 8 keys x 8 dims block in registers.
+// row; V transposed, row `dim` of Wp key positions, position chunk j at chunk
+// j ^ (dim mod 16), each thread transposing an 8 keys x 8 dims block in registers.  In
+// each 32-key block, position chunk g (g = 0..3) holds keys 4 g .. 4 g + 3 and
+// 16 + 4 g .. 16 + 4 g + 3: the keys whose scores lane group g holds after S^T (two
+// 16-key tiles), so P^T of 32 keys is one 16 x 16 x 32 MFMA operand.
 // Every load of a thread (at most KV / 4096 K chunks and one 8 x 8 V block, Wp D <= KV)
 // is issued before the first LDS write, so staging costs one memory round trip.
 template <int D, int KV>
@@ -467,7 +470,7 @@ __device__ __forceinline__ void pf_stage(const bf16* __restrict__ kc, const bf16
   uint4 vv[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const int key = kw0 + kb * 8 + r;
+    const int key = kw0 + (kb >> 2) * 32 + (kb & 3) * 4 + (r & 3) + (r >> 2) * 16;
     const bool ok = vblk && key < S;
     vv[r] = ld_once(vc + head + (ok ? (size_t)key * D + cv * 8 : 0));
     okm |= (uint32_t)ok << (NK + r);
@@ -527,27 +530,38 @@ __device__ __forceinline__ void pf_load_q(const bf16* __restrict__ q, int b, int
                     : bf16x8{};
 }
 
+// S^T for keys k0 .. k0 + 31 (window-local k0 - kw0): st[t2][r] = score(key k0 + 16 t2 +
+// 4 fg + r, query qi).  The K fragments are read before the first MFMA.
+template <int D>
+__device__ __forceinline__ void pf_scores(f32x4 (&st)[2], const bf16x8 (&qb8)[D / 32], const bf16* Ks,
+                                          int kl0, int fr, int fg) {
+  constexpr int NCH = D / 8, RPB = 128 / D;
+  bf16x8 kf[2][D / 32];
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+    const int key = kl0 + t2 * 16 + fr;            // A-operand row of this lane
+    const int sw = (key / RPB) & (NCH - 1);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      kf[t2][c] = *reinterpret_cast<const bf16x8*>(&Ks[key * D + (((c * 4 + fg) ^ sw) << 3)]);
+  }
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+    st[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) st[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t2][c], qb8[c], st[t2], 0, 0, 0);
+  }
+}
+
 // Keys k_begin .. k_end - 1 (k_begin a multiple of 32, inside the window staged at
 // kw0 with Wp padded keys) for this lane's query qi.
 template <int D>
 __device__ __forceinline__ void pf_keys(PfBlock<D>& s, const bf16x8 (&qb8)[D / 32], const bf16* Ks,
                                         const bf16* Vt, int kw0, int Wp, int k_begin, int k_end, int qi,
                                         int S, int fr, int fg) {
-  constexpr int NCH = D / 8, RPB = 128 / D;
   for (int k0 = k_begin; k0 < k_end; k0 += 32) {
-    // S^T for keys k0 .. k0 + 31: st[t2][r] = score(key k0 + 16 t2 + 4 fg + r, query qi)
     f32x4 st[2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      st[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = k0 - kw0 + t2 * 16 + fr;     // A-operand row of this lane (window-local)
-      const int sw = (key / RPB) & (NCH - 1);
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[key * D + (((c * 4 + fg) ^ sw) << 3)]);
-        st[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qb8[c], st[t2], 0, 0, 0);
-      }
-    }
+    pf_scores<D>(st, qb8, Ks, k0 - kw0, fr, fg);
     float cm = -INFINITY;
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
@@ -564,26 +578,27 @@ __device__ __forceinline__ void pf_keys(PfBlock<D>& s, const bf16x8 (&qb8)[D / 3
     s.lsum *= sc;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) s.oacc[t] *= sc;
+    // P^T of the 32 keys as the B operand of one 16 x 16 x 32 MFMA: this lane's eight
+    // keys are 4 fg .. 4 fg + 3 (tile 0) and 16 + 4 fg .. + 3 (tile 1), position chunk fg
+    // of the block in V^T
+    bf16x8 ph, pl;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      bf16x4 ph, pl;
+    for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = st[t2][r] == -INFINITY ? 0.f : __expf(st[t2][r] - mn);
         s.lsum += p;
         const bf16 hi = f2bf(p);
-        ph[r] = bf_bits(hi);
-        pl[r] = bf_bits(f2bf(p - bf2f(hi)));
+        ph[t2 * 4 + r] = __builtin_bit_cast(__bf16, hi);
+        pl[t2 * 4 + r] = __builtin_bit_cast(__bf16, f2bf(p - bf2f(hi)));
       }
-      // V^T fragment: dim 16 t + fr, keys k0 + 16 t2 + 4 fg .. + 4 (half a swizzled chunk)
-      const int chunk = ((k0 - kw0 + t2 * 16) >> 3) + (fg >> 1);
+    const int chunk = ((k0 - kw0) >> 3) + fg;
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const int dim = t * 16 + fr;
-        const bf16x4 va = *reinterpret_cast<const bf16x4*>(&Vt[dim * Wp + ((chunk ^ (dim & 15)) << 3) + ((fg & 1) << 2)]);
-        s.oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, s.oacc[t], 0, 0, 0);
-        s.oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, s.oacc[t], 0, 0, 0);
-      }
+    for (int t = 0; t < D / 16; ++t) {
+      const int dim = t * 16 + fr;
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vt[dim * Wp + ((chunk ^ (dim & 15)) << 3)]);
+      s.oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, s.oacc[t], 0, 0, 0);
+      s.oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, s.oacc[t], 0, 0, 0);
     }
   }
 }
@@ -729,7 +744,9 @@ void launch_attn_prefill(int dt, const void* q, const void* k_cache, const void*
                          int B, int S, int H, int D, int S_max, int o_il, hipStream_t st) {
   if (dt == DT_BF16 && (D == 32 || D == 64 || D == 128) && pf_pad(S, D)) {
     // Heads whose keys fit in two windows of half the LDS take 64 KB per WG, so two WGs
-    // share a CU and one stages its head while the other computes.
+    // share a CU and one stages its head while the other computes.  (At 128 dims that
+    // costs register spills; one full window per WG, which needs none, measured slower
+    // in the prompt pass all the same: 175.0 against 157.8 us per layer at S 256.)
     const bool half = pf_pad(S, D, kPfKV / 2) != 0;
     const int sp = half ? pf_pad(S, D, kPfKV / 2) : pf_pad(S, D);
 #define HE_PF(DD, KV)                                                                                 \
