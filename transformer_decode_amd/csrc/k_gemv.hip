@@ -60,29 +60,36 @@ GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole, 
   const int nrb = N / 16, frmax = p.mt <= 4 ? 4 : 2;
   if (p.mt >= 8 && !f8) {
     // 65..128 batch rows: each k-step a wave reads 2 KB of activations from L2 per 16
-    // weight rows it owns, so waves take 48-64 rows (accumulators in 96-128 registers,
-    // one wave per SIMD).  Measured at the 13B decode shapes, batch 128 (per launch):
-    // QKV 58.6 -> 43.1 us, out 24.8 -> 19.3, FC1 77.2 -> 64.0, FC2 88.8 -> 62.6.
+    // weight rows it owns, so waves take 48-80 rows (accumulators in up to 160
+    // registers, one wave per SIMD) and the grid one WG per CU.  Measured at the 13B
+    // decode shapes, batch 128 (per launch, from the plans for up to 64 rows): QKV
+    // 58.6 -> 43.4 us, out 24.8 -> 19.2, FC1 77.2 -> 47.0, FC2 88.8 -> 47.1.
     auto rows = [&](int fr) { return (long)(nrb + fr - 1) / fr; };
     if (whole && rows(2) >= 1024) {        // the LM head: 64 rows and the whole K per wave
       p.fr = 4; p.nwk = 1; p.kr = K; p.splits = 1;   // (batch 128, K 5120: 198.5 -> 135.3 us)
       return p;
     }
     if (whole || N > K) {                  // QKV (fused epilogue) and FC1 (ReLU epilogue): whole K
-      int fr = 4;
-      if ((rows(3) + 255) / 256 * 3 < (rows(4) + 255) / 256 * 4) fr = 3;
+      int fr = 5;                          // the fewest rounds of 256 WGs times rows per wave
+      long best = -1;
+      for (int f : {5, 4, 3}) {
+        const long cost = (rows(f) + 255) / 256 * f;
+        if (best < 0 || cost < best) { best = cost; fr = f; }
+      }
       int nwk = 1;
       while (nwk < 4 && rows(fr) * nwk < 1024 && K % (128 * nwk * 2) == 0) nwk *= 2;
       if (K % (128 * nwk) == 0) {
         p.fr = fr; p.nwk = nwk; p.kr = K / nwk; p.splits = 1;
         return p;
       }
-    } else if (allow_split) {              // out-proj, FC2: two or more partial groups of 4 waves
-      for (int slices = 4; slices <= 64; slices += 4)
-        if (K % slices == 0 && (K / slices) % 128 == 0 && rows(3) * slices >= 512) {
-          p.fr = 3; p.nwk = 4; p.kr = K / slices; p.splits = slices / 4;
-          return p;
-        }
+    } else if (allow_split) {              // out-proj, FC2: the fewest partial groups that
+      const long rg = rows(5);             // give 256 WGs, each with the most waves that divide K
+      for (int sp = (int)std::max<long>(1, (256 + rg - 1) / rg); sp <= 64; ++sp)
+        for (int nwk : {4, 2, 1})
+          if (K % (sp * nwk * 128) == 0) {
+            p.fr = 5; p.nwk = nwk; p.kr = K / (sp * nwk); p.splits = sp;
+            return p;
+          }
     }
   }
   auto choose = [&](int kr, bool need_waves) {
@@ -466,6 +473,12 @@ static void il_launch_nwk(int out, const bf16* X, const bf16* W, const IlArgs& a
 template <int MT>
 static void il_launch_fr(int out, const bf16* X, const bf16* W, const IlArgs& a, const GemvPlan& p,
                          hipStream_t st) {
+  if constexpr (MT == 8) {            // five fragments per wave: the 65-128-row plans only
+    if (p.fr == 5) {
+      il_launch_nwk<MT, 5>(out, X, W, a, p, st);
+      return;
+    }
+  }
   if (p.fr == 4) il_launch_nwk<MT, 4>(out, X, W, a, p, st);
   else if (p.fr == 3) il_launch_nwk<MT, 3>(out, X, W, a, p, st);
   else if (p.fr >= 2) il_launch_nwk<MT, 2>(out, X, W, a, p, st);
