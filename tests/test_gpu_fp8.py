@@ -117,6 +117,13 @@ def test_opt125m_fp8_decode_matches_oracle():
     _decode_parity(wl, rows=[0, wl.batch - 1], steps=[0, 1, 5, 31])
 
 
+def test_opt125m_fp8_decode_batch_100():
+    """100 batch rows: activation tiles of 128 rows, 100 live, with E4M3 weights (the
+    plans for 65-128 rows of the FP8 path)."""
+    wl = dataclasses.replace(synth.WORKLOADS["opt125m"], batch=100, prompt_len=64, gen_len=16, max_seq=80)
+    _decode_parity(wl, rows=[0, 63, 64, 99], steps=[0, 1, 8, 15])
+
+
 def test_opt6_7b_shape_fp8_decode_matches_oracle():
     """Two layers of the 6.7B shape at the full batch of 64: the bench's decode plans."""
     wl = synth.WORKLOADS["opt6.7b"]
