@@ -454,6 +454,7 @@ template <int D, int KV>
 __device__ __forceinline__ void pf_stage(const bf16* __restrict__ kc, const bf16* __restrict__ vc,
                                          size_t head, int S, int kw0, int Wp, bf16* Ks, bf16* Vt, int tid) {
   constexpr int NCH = D / 8, RPB = 128 / D, NK = (KV / 8 + 511) / 512;
+  static_assert(NK + 8 <= 32, "the validity bits of a thread's loads fit one word");
   // loads without branches: a slot past the keys reads the head's first row (always
   // present) and is zeroed where it is written, so the loads issue back to back
   uint4 kv[NK];

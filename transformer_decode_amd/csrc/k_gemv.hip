@@ -49,7 +49,8 @@ int decode_mt(int M) { return pow2_ceil((M + 15) / 16); }
 // as keeps the WG count a multiple of the 256 CUs or >= 1024.  `whole` asks for a
 // single partial group (the fused bias+ReLU and argmax epilogues).  `f8` (E4M3
 // weights) asks for K ranges that are multiples of 256 (eight k-steps per loop
-// iteration).  fp32: a split over K.
+// iteration).  65-128 batch rows (bf16 weights) follow their own rules, below.
+// fp32: a split over K.
 GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole, bool f8) {
   GemvPlan p;
   if (dt != DT_BF16) {
@@ -66,7 +67,7 @@ GemvPlan decode_plan(int dt, int M, int N, int K, bool allow_split, bool whole, 
     // 58.6 -> 43.4 us, out 24.8 -> 19.2, FC1 77.2 -> 47.0, FC2 88.8 -> 47.1.
     auto rows = [&](int fr) { return (long)(nrb + fr - 1) / fr; };
     if (whole && rows(2) >= 1024) {        // the LM head: 64 rows and the whole K per wave
-      p.fr = 4; p.nwk = 1; p.kr = K; p.splits = 1;   // (batch 128, K 5120: 198.5 -> 135.3 us)
+      p.fr = 4; p.nwk = 1; p.kr = K; p.splits = 1;   // (batch 128, K 5120: 199.5 -> 141.1 us)
       return p;
     }
     if (whole || N > K) {                  // QKV (fused epilogue) and FC1 (ReLU epilogue): whole K
