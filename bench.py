@@ -252,7 +252,7 @@ def timeline_summary(trace_csv, workload, command):
     steps = []
     for a, b in zip(opens, opens[1:]):
         names = [rows[i]["Kernel_Name"] for i in range(a, b)]
-        if any("gemv_il" in n for n in names) and not any("gemm_frag" in n for n in names):
+        if any("gemv_il" in n for n in names) and not any("gemm_" in n for n in names):
             steps.append((a, b))
     if steps:   # whole steps only: the interval that spans a generation's end holds other work
         from collections import Counter
