@@ -1,8 +1,8 @@
 // Prompt-pass projections of libhe: Y[M,N] = X[M,K] W[N,K]^T with fused epilogues.
 //
 // bf16 models: for M, N multiples of 256 an MFMA GEMM on 32 x 32 x 16 tiles with
-// 256 x 256 macro tiles staged by LDS DMA, persistent (gemm_pers_kernel) when K is a
-// multiple of 128, else one tile per WG (gemm_frag_kernel); other shapes run a
+// 256 x 256 macro tiles staged by LDS DMA, one persistent WG per CU (gemm_pers_kernel,
+// K a multiple of 128: every model the library accepts); other shapes run a
 // 256 x 256 (8 waves) or 128 x 128 (4 waves) kernel on 16 x 16 x 32 tiles with
 // register-staged loads.  fp32 models (the tiny workload only): a plain tiled FMA
 // kernel.  All end in the same epilogue: bias, q scaling + KV-cache scatter (the
@@ -393,214 +393,29 @@ __device__ __forceinline__ uint32_t frag_step_part(int s, int K, int il) {
 // while the other waits at the stage barrier or for its LDS reads (measured 3 to 4%
 // faster than four waves of 128 x 128 with one wave per SIMD on the 6.7B prompt-pass
 // shapes, 11% on K = 1024 shapes).  Each wave loads two X and two W fragments per stage;
-// per 16-wide k-step it reads 2 W and 4 X operands for 8 MFMAs.
-template <int MODE, bool WIL, bool XIL>
-__global__ __launch_bounds__(512) void gemm_frag_kernel(const bf16* __restrict__ X,
-                                                         const bf16* __restrict__ W, int M, int N,
-                                                         int K, EpiArgs e) {
-  __shared__ __attribute__((aligned(1024))) bf16 fsm[FST * 2 * 16 * 512];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 2, wn = wv & 3;
-
-  const int nm = M / FBM, nn = N / FBN, T = nm * nn;
-  const int per = (T + 7) / 8;
-  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (t >= T) return;
-  constexpr int GM = 4;
-  const int group = t / (GM * nn), first_m = group * GM;
-  const int gsz = min(nm - first_m, GM);
-  const int tm = first_m + (t % (GM * nn)) % gsz, tn = (t % (GM * nn)) / gsz;
-  const int m0 = tm * FBM, n0 = tn * FBN;
-  const int ilx = XIL ? e.x_il : 0, ilw = WIL ? e.w_il : 0;
-  const uint32_t tile_bytes = (uint32_t)(FBM * K * 2);
-  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(X + (size_t)m0 * K, tile_bytes);
-  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W + (size_t)n0 * K, tile_bytes);
-  // this wave's DMA: 16-row fragments 2 wv and 2 wv + 1 of each operand
-  const uint32_t lane_x = frag_lane_part(lane, K, ilx), lane_w = frag_lane_part(lane, K, ilw);
-  uint32_t vx[2], vw[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t rows = (uint32_t)((wv * 2 + q) * 16 * K);
-    vx[q] = (lane_x + rows) * 2;
-    vw[q] = (lane_w + rows) * 2;
-  }
-  // DMA g (0..3): fragment 2 wv + g / 2 of X (g even) or W (g odd)
-  auto dma = [&](int g, int s, int buf) {
-    bf16* sa = fsm + (size_t)buf * 2 * 16 * 512 + (wv * 2 + (g >> 1)) * 512;
-    if ((g & 1) == 0)
-      buf_dma16(rx, sa, vx[g >> 1], frag_step_part(s, K, ilx) * 2);
-    else
-      buf_dma16(rw, sa + 16 * 512, vw[g >> 1], frag_step_part(s, K, ilw) * 2);
-  };
-  auto issue = [&](int s, int buf) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) dma(g, s, buf);
-  };
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // operand g of k-step ks of stage s: g < 2 column tile 2 wn + g of W, else row tile
-  // 4 wm + g - 2 of X.  The 32 x 32 x 16 operand (lane l: row l % 32, k 8 (l / 32) .. + 8
-  // of the step) of 32-row tile t is gathered from the 16-row fragments 2t and 2t + 1:
-  // row r sits in fragment 2t + r / 16 at lane (r mod 16) + 16 (2 ks + l / 32), so each
-  // 16 lanes read 256 consecutive bytes, free of bank conflicts.
-  const int rl = lane & 31;
-  const uint32_t lane_lds = (uint32_t)((rl >> 4) * 512 + ((rl & 15) + ((lane >> 5) << 4)) * 8);
-  auto read_frag = [&](int s, int ks, int g) -> bf16x8 {
-    const bf16* sa = fsm + (size_t)(s & (FST - 1)) * 2 * 16 * 512 + ks * 256 + lane_lds;
-    return g < 2 ? *reinterpret_cast<const bf16x8*>(sa + 16 * 512 + (wn * 2 + g) * 1024)
-                 : *reinterpret_cast<const bf16x8*>(sa + (wm * 4 + g - 2) * 1024);
-  };
-  // group g of a half-stage: MFMAs of row tile g with column tiles 0 and 1
-  auto mma2 = [&](const bf16x8 (&r)[6], int g) {
-    acc[g][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[0], r[2 + g], acc[g][0], 0, 0, 0);
-    acc[g][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[1], r[2 + g], acc[g][1], 0, 0, 0);
-  };
-  // reads of group g: operands g (g < 2), then 2 and 3 (g = 2), 4 and 5 (g = 3)
-  auto reads = [&](bf16x8 (&r)[6], int s, int ks, int g) {
-    if (g < 2) {
-      r[g] = read_frag(s, ks, g);
-    } else {
-      r[2 * g - 2] = read_frag(s, ks, 2 * g - 2);
-      r[2 * g - 1] = read_frag(s, ks, 2 * g - 1);
-    }
-  };
-
-  // The loop body is straight-line so the accumulators stay in place.  Each half-stage
-  // is four groups of one DMA issue, one or two LDS reads and two MFMAs, in that order,
-  // so the DMA issues and the reads of the next k-step are spread between the MFMAs
-  // rather than queued in front of them.  r0 holds the first 16-wide k-step of a stage,
-  // r1 the second; each is read one half-stage before its MFMAs.  Every iteration issues
-  // one stage of DMA (the last FST - 1 repeat the final stage's addresses into the free
-  // buffer, never read again) and the last stage re-reads its own first k-step.
-  const int ns = K / 32;
-#pragma unroll
-  for (int s = 0; s < FST - 1; ++s) issue(min(s, ns - 1), s);
-  HE_WAIT_VMCNT(4 * (FST - 2));
-  barrier_keep_loads();
-  bf16x8 r0[6], r1[6];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) reads(r0, 0, 0, g);
-  for (int s = 0; s < ns; ++s) {
-    // half A: refill the buffer stage s - 1 used (every wave read it before the last
-    // barrier), read the second k-step of stage s, multiply the first
-    const int sd = min(s + FST - 1, ns - 1), bd = (s + FST - 1) & (FST - 1);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      dma(g, sd, bd);
-      reads(r1, s, 1, g);
-      mma2(r0, g);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // stage s + 1 must have landed here and in every wave before it is read
-    HE_WAIT_VMCNT(4 * (FST - 2));
-    barrier_keep_loads();
-    // half B: read the first k-step of stage s + 1, multiply the second of stage s
-    const int sn = s + 1 < ns ? s + 1 : s;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      reads(r0, sn, 0, g);
-      mma2(r1, g);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  HE_WAIT_VMCNT(0);
-  barrier_keep_loads();
-
-  // Epilogue through LDS (free after the last barrier), one 32-row tile at a time: the
-  // MFMAs compute W X^T per tile, so lane l holds output row l % 32 and register 4 q + c
-  // holds column 8 q + 4 (l / 32) + c; each wave parks 32 rows x 64 columns (fp32, rows
-  // padded to 68 words: conflict-free 16-byte writes) in its own region, then reads them
-  // back as 8 consecutive columns per lane, so 8 lanes cover a row and every store is a
-  // 16- or 32-byte access to whole row segments.
-  constexpr int PR = 68;
-  float* park = reinterpret_cast<float*>(fsm) + (size_t)wv * 32 * PR;
-  if constexpr (MODE == EPI_RESID) {
-    // h += acc + bias: the stream rows of 32-row slice i + 1 are fetched while slice i
-    // is added and stored, so the slices' HBM round trips overlap.  Lane l covers rows
-    // l / 8 + 8 it of a slice and the same 8 columns throughout (one bias load).
-    const int col = (lane & 7) << 3, n = n0 + wn * 64 + col;
-    float bias[8];
-    if (e.bias) load8((const bf16*)e.bias + n, bias);
-    else
-#pragma unroll
-      for (int c = 0; c < 8; ++c) bias[c] = 0.f;
-    auto hrow = [&](int i, int it) { return e.h + (size_t)(m0 + wm * 128 + i * 32 + (lane >> 3) + 8 * it) * N + n; };
-    float hc[4][8], hn[4][8];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) load8(hrow(0, it), hc[it]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4*>(park + rl * PR + j * 32 + q * 8 + ((lane >> 5) << 2)) =
-              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-      __builtin_amdgcn_s_waitcnt(0xC07F);       // the slice is parked (lgkmcnt(0))
-      if (i < 3)
-#pragma unroll
-        for (int it = 0; it < 4; ++it) load8(hrow(i + 1, it), hn[it]);
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int row = (lane >> 3) + 8 * it;
-        const float4 v0 = *reinterpret_cast<const float4*>(park + row * PR + col);
-        const float4 v1 = *reinterpret_cast<const float4*>(park + row * PR + col + 4);
-        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        float hv[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) hv[c] = hc[it][c] + (v[c] + bias[c]);
-        store8(hrow(i, it), hv);
-      }
-      // this slice's park reads are done before the next slice parks (stores may fly)
-      __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0), vmcnt and expcnt left open
-      if (i < 3)
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) hc[it][c] = hn[it][c];
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(park + rl * PR + j * 32 + q * 8 + ((lane >> 5) << 2)) =
-            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-    __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int seg = lane + it * 64, row = seg >> 3, col = (seg & 7) << 3;
-      float v[8];
-      const float4 v0 = *reinterpret_cast<const float4*>(park + row * PR + col);
-      const float4 v1 = *reinterpret_cast<const float4*>(park + row * PR + col + 4);
-      v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-      epi_store8<MODE>(e, m0 + wm * 128 + i * 32 + row, n0 + wn * 64 + col, N, v);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-}
-
-// Persistent form: one WG per CU walks its tiles (the same tiles, in the same order, as
-// the one-tile-per-WG launch gives a CU).  The stage stream runs on across tiles: the
+// per 16-wide k-step it reads 2 W and 4 X operands for 8 MFMAs.  Operand g of k-step ks
+// of a stage: g < 2 column tile 2 wn + g of W, else row tile 4 wm + g - 2 of X; the
+// 32 x 32 x 16 operand (lane l: row l % 32, k 8 (l / 32) .. + 8 of the step) of 32-row
+// tile t is gathered from the 16-row fragments 2t and 2t + 1 (row r in fragment
+// 2t + r / 16 at lane (r mod 16) + 16 (2 ks + l / 32)), so each 16 lanes read 256
+// consecutive bytes, free of bank conflicts.
+//
+// The loop body is straight-line so the accumulators stay in place.  Each half-stage is
+// four groups of one DMA issue, one or two LDS reads and two MFMAs, in that order, so
+// the DMA issues and the reads of the next k-step are spread between the MFMAs rather
+// than queued in front of them.  r0 holds the first 16-wide k-step of a stage, r1 the
+// second; each is read one half-stage before its MFMAs.
+//
+// Persistent: one WG per CU walks its tiles (the same tiles, in the same order, as a
+// launch of one WG per tile would give that CU).  The stage stream runs on across tiles: the
 // last three k-stages of tile r issue the DMA of tile r + 1's stages 0..2 (K / 32 is a
 // multiple of 4, so stage s of every tile keeps buffer s mod 4), and the epilogue of tile
 // r runs while they land.  The epilogue parks 32 x 32 blocks in the fourth buffer (held
 // by tile r's last stage, free after its last barrier): 4 KB per wave, 16-byte chunks
 // XOR-swizzled by row so that the parking writes and the row-wise reads hit distinct
-// banks.  The arithmetic per element is the one-tile kernel's (bit-identical results).
-// Measured at the OPT-6.7B prompt-pass shapes: QKV 1196.5 -> 1151.2 us, FC1 1587.1 ->
-// 1522.1, out 458.4 -> 447.0; the WG relaunch and the pipeline fill per tile are gone.
+// banks.  Against one WG per tile (the same arithmetic, bit-identical results), measured
+// at the OPT-6.7B prompt-pass shapes: QKV 1196.5 -> 1151.2 us, FC1 1587.1 -> 1522.1, out
+// 458.4 -> 447.0.
 template <int MODE, bool WIL, bool XIL>
 __global__ __launch_bounds__(512) void gemm_pers_kernel(const bf16* __restrict__ X,
                                                          const bf16* __restrict__ W, int M, int N,
@@ -848,29 +663,19 @@ template <int MODE>
 static void gemm_dispatch(int dt, const void* X, const void* W, int M, int N, int K,
                           const EpiArgs& e, hipStream_t st) {
   if (dt == DT_BF16) {
-    if (M % FBM == 0 && N % FBN == 0 && K % 32 == 0) {
-      const int blocks = ((M / FBM) * (N / FBN) + 7) / 8 * 8;
+    if (M % FBM == 0 && N % FBN == 0 && K % (32 * FST) == 0) {
+      // one WG per CU (at most 32 per XCD), each walking ceil(tiles / 8) / 32 tiles
+      const int per = ((M / FBM) * (N / FBN) + 7) / 8;
+      const int pb = 8 * std::min(per, 32);
       const bf16 *x = (const bf16*)X, *w = (const bf16*)W;
-      if ((K / 32) % FST == 0) {     // persistent: one WG per CU, at most 32 per XCD
-        const int pb = 8 * std::min(blocks / 8, 32);
-        if (e.w_il && e.x_il)
-          gemm_pers_kernel<MODE, true, true><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
-        else if (e.w_il)
-          gemm_pers_kernel<MODE, true, false><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
-        else if (e.x_il)
-          gemm_pers_kernel<MODE, false, true><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
-        else
-          gemm_pers_kernel<MODE, false, false><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
-        return;
-      }
       if (e.w_il && e.x_il)
-        gemm_frag_kernel<MODE, true, true><<<blocks, 512, 0, st>>>(x, w, M, N, K, e);
+        gemm_pers_kernel<MODE, true, true><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
       else if (e.w_il)
-        gemm_frag_kernel<MODE, true, false><<<blocks, 512, 0, st>>>(x, w, M, N, K, e);
+        gemm_pers_kernel<MODE, true, false><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
       else if (e.x_il)
-        gemm_frag_kernel<MODE, false, true><<<blocks, 512, 0, st>>>(x, w, M, N, K, e);
+        gemm_pers_kernel<MODE, false, true><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
       else
-        gemm_frag_kernel<MODE, false, false><<<blocks, 512, 0, st>>>(x, w, M, N, K, e);
+        gemm_pers_kernel<MODE, false, false><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
       return;
     }
     const long big_tiles = (long)((M + LBM - 1) / LBM) * ((N + LBN - 1) / LBN);
