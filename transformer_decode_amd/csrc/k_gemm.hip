@@ -659,14 +659,29 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     }
 }
 
+// Compute units of the current device (cached per device): the persistent GEMM puts at
+// most one WG on each.
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int MODE>
 static void gemm_dispatch(int dt, const void* X, const void* W, int M, int N, int K,
                           const EpiArgs& e, hipStream_t st) {
   if (dt == DT_BF16) {
     if (M % FBM == 0 && N % FBN == 0 && K % (32 * FST) == 0) {
-      // one WG per CU (at most 32 per XCD), each walking ceil(tiles / 8) / 32 tiles
+      // one WG per CU, a multiple of 8 (WG i runs on XCD i mod 8), each walking its
+      // XCD's tiles with stride pb / 8
       const int per = ((M / FBM) * (N / FBN) + 7) / 8;
-      const int pb = 8 * std::min(per, 32);
+      const int pb = 8 * std::min(per, std::max(1, device_cus() / 8));
       const bf16 *x = (const bf16*)X, *w = (const bf16*)W;
       if (e.w_il && e.x_il)
         gemm_pers_kernel<MODE, true, true><<<pb, 512, 0, st>>>(x, w, M, N, K, e);
