@@ -218,6 +218,50 @@ def mfma_summary(csv_path, workload, command):
     return "\n".join(lines) + "\n"
 
 
+# One --pmc pass (8 SQ counters): how busy the LDS and the MFMA pipes are per kernel class.
+OCC_COUNTERS = ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL",
+                "SQ_BUSY_CU_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES")
+
+
+def occupancy_summary(csv_path, workload, command, n_cu=256):
+    """Per kernel class, from one rocprofv3 --pmc pass of OCC_COUNTERS: the counters summed
+    over the class's dispatches, and ratios to SQ_BUSY_CU_CYCLES (summed over the CUs, so
+    busy cycles / CUs / kernel time is the clock the kernels ran at).  MFMA busy cycles are
+    counted per SIMD, so their ratio is divided by the 4 SIMDs of a CU."""
+    import csv
+    disp = {}
+    for r in csv.DictReader(open(csv_path)):
+        d = disp.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                               "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    cls = {}
+    for d in disp.values():
+        c = kernel_class(d["name"])
+        if c == "other":
+            continue
+        e = cls.setdefault(c, {"n": 0, "ns": 0.0})
+        e["n"] += 1
+        e["ns"] += d["ns"]
+        for k in OCC_COUNTERS:
+            e[k] = e.get(k, 0.0) + d.get(k, 0.0)
+    lines = [f"# LDS and MFMA activity, {workload}", "", "Command (run from the repository root, output under "
+             "gpurun_out/):", "", "```", command, "```", "",
+             "Per kernel class, summed over its dispatches of the run. busy = SQ_BUSY_CU_CYCLES (summed over "
+             f"the {n_cu} CUs); clock = busy / CUs / kernel time (meaningful for kernels that keep every CU busy; "
+             "it reads low for the 64-WG decode norms in embed_norm); LDS active = SQ_LDS_IDX_ACTIVE / busy; bank "
+             "conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; FIFO full = SQ_LDS_DATA_FIFO_FULL / busy; "
+             "MFMA busy per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / busy / 4.", "",
+             "| class | dispatches | avg us | clock (GHz) | LDS active | bank conflicts | LDS data FIFO full | "
+             "MFMA busy per SIMD |", "|---|---|---|---|---|---|---|---|"]
+    for c, e in sorted(cls.items(), key=lambda kv: -kv[1]["ns"]):
+        busy = e["SQ_BUSY_CU_CYCLES"] or 1.0
+        lines.append(f"| {c} | {e['n']} | {e['ns'] / e['n'] / 1e3:.1f} | {busy / n_cu / e['ns']:.2f} | "
+                     f"{e['SQ_LDS_IDX_ACTIVE'] / busy:.3f} | "
+                     f"{e['SQ_LDS_BANK_CONFLICT'] / max(1.0, e['SQ_LDS_IDX_ACTIVE']):.3f} | "
+                     f"{e['SQ_LDS_DATA_FIFO_FULL'] / busy:.3f} | {e['SQ_VALU_MFMA_BUSY_CYCLES'] / busy / 4:.3f} |")
+    return "\n".join(lines) + "\n"
+
+
 def stats_summary(stats_csv, workload, command):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
@@ -395,6 +439,9 @@ def main():
                     help="write the decode-step dispatch timeline of a rocprofv3 kernel trace")
     ap.add_argument("--mfma-summary", nargs=2, metavar=("MFMA_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --pmc pass of the MFMA counters into a markdown summary (no GPU)")
+    ap.add_argument("--occupancy-summary", nargs=2, metavar=("PMC_CSV", "OUT_MD"),
+                    help="turn a rocprofv3 --pmc pass of the LDS / MFMA activity counters into a markdown "
+                         "summary (no GPU)")
     ap.add_argument("--command", default="", help="the command that produced the csv (recorded; "
                     "default: the standard profiling command for the summary being written)")
     args = ap.parse_args()
@@ -422,6 +469,16 @@ def main():
             f"python3 bench.py --workload {args.workload} --mfma-summary {m_csv} {o}")
         with open(o, "w") as fh:
             fh.write(mfma_summary(m_csv, args.workload, cmd))
+        return
+    if args.occupancy_summary:
+        p_csv, o = args.occupancy_summary
+        cmd = args.command or (
+            f"export TMPDIR=/tmp && "
+            f"timeout -s KILL 120 rocprofv3 --pmc {' '.join(OCC_COUNTERS)} -f csv -d gpurun_out/pmc_lds -o lds -- "
+            f"python3 bench.py --workload {args.workload} --trace-steps 3 && "
+            f"python3 bench.py --workload {args.workload} --occupancy-summary {p_csv} {o}")
+        with open(o, "w") as fh:
+            fh.write(occupancy_summary(p_csv, args.workload, cmd))
         return
     if args.timeline_summary:
         tr_csv, o = args.timeline_summary
